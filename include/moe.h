@@ -1,0 +1,173 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer forward library (libmoe.so).
+ *
+ * The layer, as the vLLM fused-MoE config page describes it (page "MoE 的隐藏加速开关：
+ * 那些按显卡命名的 config 到底是什么", section 02, the Tokens -> Router -> Grouped GEMM ->
+ * weighted-sum diagram):
+ *   1. route:   logits = hidden . W_r^T (+ bias); each token keeps its top-k experts
+ *               (descending logit, exact ties to the lower expert id) with gate weights
+ *               softmax(kept logits);
+ *   2. permute: the T*k (token, slot) assignments are grouped by expert in the stable
+ *               order of (expert, token, slot);
+ *   3. experts: every assignment runs its expert's SwiGLU FFN,
+ *               y = (silu(x Wg^T) * (x Wu^T)) Wd^T, as one grouped GEMM whose tiles each
+ *               fetch their own expert's weights;
+ *   4. combine: out[t] = sum_j w[t,j] * y[t,j]  (+ shared-expert output, weight 1).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host).  Every tensor is row-major,
+ *     contiguous and 16-byte aligned; the workspace is 256-byte aligned.
+ *   - Calls are asynchronous and ordered on the given stream.  None allocates, frees or
+ *     synchronizes, except moe_last_device_error, which synchronizes its stream.
+ *   - Arguments are validated on the host before anything is enqueued; on any error a
+ *     status code is returned and nothing is enqueued.  Nothing throws across the ABI.
+ *   - A call with T == 0 validates the problem, enqueues nothing and returns MOE_OK; its
+ *     tensor pointers may then be NULL.
+ *   - The caller owns every buffer, including the workspace.  The library keeps no
+ *     per-call state outside the workspace (only a cache of device properties).
+ *   - Calls that share one workspace must not run concurrently (on different streams);
+ *     each call leaves the workspace's control block ready for the next call, so
+ *     back-to-back calls and hipGraph replays need no reset.
+ *   - Results are bitwise reproducible for a fixed build, device and input, whatever the
+ *     launch grid or the order in which work items are taken.
+ *
+ * Layouts (E routed experts, d hidden, n expert intermediate, k top-k, T tokens):
+ *   hidden   [T, d]     act dtype          out [T, d] act dtype (must not alias hidden)
+ *   w_router [E, d]     act dtype          one row per expert
+ *   bias     [E]        float32 or NULL    added to the logits
+ *   w_gate   [E, n, d]  weight dtype       one row per intermediate channel
+ *   w_up     [E, n, d]  weight dtype
+ *   w_down   [E, d, n]  weight dtype       one row per output channel
+ *   fp8 block scales (weight dtype MOE_FP8_E4M3, scale_block = 128), one float32 per
+ *   128x128 block of each [rows, cols] matrix:  s_gate, s_up [E, n/128, d/128],
+ *   s_down [E, d/128, n/128]; W[i,j] = e4m3(q[i,j]) * s[i/128, j/128]
+ *   (the fp8_w8a8 + block_shape [128,128] weights named in section 03 of the same page).
+ *   shared expert (n_shared = 1): sh_gate, sh_up [n, d], sh_down [d, n] and, for fp8,
+ *   sh_s_gate, sh_s_up [n/128, d/128], sh_s_down [d/128, n/128]; it has weight 1 and
+ *   runs on every token (GC-MoE article, "two MMA implementations": fused shared experts).
+ *
+ * Supported (act dtype, weight dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ * Shape limits: 1 <= k <= E <= 1024, d and n multiples of 256, T*k < 2^31.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad shape, k > E, ...        */
+  MOE_ERR_UNSUPPORTED = 2,        /* legal but not implemented: dtype combo, shape limits  */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,/* ws_bytes < moe_workspace_size()                        */
+  MOE_ERR_HIP = 4,                /* a HIP runtime call (launch, device query) failed       */
+  MOE_ERR_DEVICE_FAULT = 5,       /* a device-side wait timed out, or the workspace was not
+                                     initialised with moe_workspace_init                   */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 /* OCP e4m3fn */ } moe_dtype;
+
+/* (host) problem descriptor; dtype fields hold moe_dtype values. */
+typedef struct {
+  int64_t T;          /* tokens in this call (the M of the grouped GEMM), T >= 0         */
+  int32_t d;          /* hidden size                                                      */
+  int32_t n;          /* expert intermediate size                                         */
+  int32_t E;          /* routed experts                                                   */
+  int32_t k;          /* experts kept per token, 1 <= k <= E                              */
+  int32_t n_shared;   /* 0 or 1 always-on shared expert                                   */
+  int32_t act_dtype;  /* MOE_F32 or MOE_BF16: hidden, w_router, out                       */
+  int32_t w_dtype;    /* MOE_F32, MOE_BF16 or MOE_FP8_E4M3: expert weights               */
+  int32_t scale_block;/* 128 when w_dtype == MOE_FP8_E4M3, else 0                         */
+} moe_problem;
+
+/* (host) struct of device pointers to the expert weights (layouts above). */
+typedef struct {
+  const void *w_gate, *w_up, *w_down;
+  const float *s_gate, *s_up, *s_down;          /* fp8 only, else NULL */
+  const void *sh_gate, *sh_up, *sh_down;        /* n_shared == 1 only, else NULL */
+  const float *sh_s_gate, *sh_s_up, *sh_s_down; /* fp8 and n_shared == 1 only */
+} moe_weights;
+
+/* (host) struct of optional device outputs of the routing and permutation; any field may
+ * be NULL.  topk_ids/topk_weights [T,k] int32/float32 (slot j = j-th largest logit),
+ * logits [T,E] float32 (bias included), counts [E], offsets [E+1] (exclusive prefix sum
+ * of counts, offsets[E] = T*k), perm [T*k] (perm[p] = t*k+j in (expert, token, slot)
+ * order) and inv_perm [T*k] (inv_perm[t*k+j] = p), all int32. */
+typedef struct {
+  int32_t *topk_ids;
+  float *topk_weights;
+  float *logits;
+  int32_t *counts, *offsets, *perm, *inv_perm;
+} moe_route_out;
+
+/* (host) optional launch controls, for tests and ablations; pass NULL for the defaults.
+ * grid_wgs: workgroups of the persistent launch (0 = CUs x occupancy).
+ * schedule: 0 = dynamic (work items taken from an atomic queue in the workspace),
+ *           1 = static (item i is bound to workgroup i mod grid, like static expert-to-SM
+ *               binding in the Weave review, section 4.2),
+ *           2 = staged (one launch per phase, the non-fused baseline of the kernel-fusion
+ *               comparison page "MoE推理优化：内核融合与分步执行方案对比", scheme B).
+ * Every schedule gives bitwise identical results. */
+typedef struct {
+  int32_t grid_wgs;
+  int32_t schedule;
+  int32_t reserved[6];
+} moe_launch_options;
+
+/* Bytes of workspace a problem needs (host only, no HIP call).  The bound depends on T*k
+ * and the shapes, never on the routing.  Returns INVALID_ARGUMENT/UNSUPPORTED like the
+ * compute calls. */
+moe_status moe_workspace_size(const moe_problem *p, size_t *bytes /* (host) out */);
+
+/* Clears the workspace's control block (a fill kernel on `stream`).  Call once after
+ * allocating a workspace, and again after a MOE_ERR_DEVICE_FAULT.  Needs at least 4096
+ * bytes. */
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Step 1 alone: router logits, top-k and gate weights.  topk_ids and topk_weights are
+ * required; logits and bias may be NULL.  Needs a workspace sized for p. */
+moe_status moe_route(const moe_problem *p, const void *hidden, const void *w_router,
+                     const float *bias, int32_t *topk_ids, float *topk_weights, float *logits,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Step 2 alone: histogram, exclusive scan and stable scatter of given top-k ids
+ * (each row of topk_ids must hold k distinct ids in [0, E)).  All outputs required. */
+moe_status moe_permute(const moe_problem *p, const int32_t *topk_ids, int32_t *counts,
+                       int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* The whole layer (steps 1-4) in one persistent launch.  route_out may be NULL. */
+moe_status moe_forward(const moe_problem *p, const void *hidden, const void *w_router,
+                       const float *bias, const moe_weights *w, void *out,
+                       const moe_route_out *route_out, void *ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* moe_forward with launch controls (opts may be NULL). */
+moe_status moe_forward_ex(const moe_problem *p, const void *hidden, const void *w_router,
+                          const float *bias, const moe_weights *w, void *out,
+                          const moe_route_out *route_out, void *ws, size_t ws_bytes,
+                          hipStream_t stream, const moe_launch_options *opts);
+
+/* Synchronizes `stream`, then reports MOE_ERR_DEVICE_FAULT if a device-side wait of an
+ * earlier call on this workspace timed out (or the workspace was never initialised),
+ * else MOE_OK.  The fault flag stays set until moe_workspace_init. */
+moe_status moe_last_device_error(const void *ws, hipStream_t stream);
+
+/* Static, never NULL. */
+const char *moe_status_string(moe_status s);
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -78,11 +78,13 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
 
 def dequant_blocks(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np.ndarray:
     """W[i, j] = decode(q[i, j]) * scale[i // block, j // block]  (float64, exact)."""
-    w = e4m3_decode(codes)
+    # decode through a 256-entry table of the code values (same definition, faster)
+    w = e4m3_decode(np.arange(256, dtype=np.uint8))[np.asarray(codes, np.uint8)]
     R, C = w.shape
-    s = np.repeat(np.repeat(np.asarray(scales, np.float64), block, axis=0), block, axis=1)
-    assert s.shape == (R, C)
-    return w * s
+    s = np.asarray(scales, np.float64)
+    assert s.shape == (R // block, C // block) and R % block == 0 and C % block == 0
+    w = w.reshape(R // block, block, C // block, block) * s[:, None, :, None]
+    return w.reshape(R, C)
 
 
 # ----------------------------------------------------------------------------

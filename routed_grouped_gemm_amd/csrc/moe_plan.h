@@ -1,0 +1,140 @@
+// moe_plan.h -- host-side problem validation, tile choice and workspace layout.
+//
+// Pure C++ (no HIP calls), so it also builds with g++ for CPU tests.  The tile choice
+// is an M-bucket table in the spirit of the per-M tile tables of the vLLM fused-MoE
+// config page (section 03: one tile setting per bucket of the step's token count M),
+// keyed here by the mean rows per routed expert, T*k/E.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kThreads = 256;          // threads per workgroup (4 wave64)
+constexpr int kWaves = 4;
+constexpr int kCtrlBytes = 4096;       // control block at the start of the workspace
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 256;
+constexpr int kLogitTokens = 16;       // router item: 16 tokens x 64 experts
+constexpr int kLogitExperts = 64;
+constexpr int kGuCols = 64;            // gate/up item: 64 H columns (16 per wave)
+constexpr int kDnCols = 128;           // down item: 128 output columns (32 per wave)
+constexpr int kCombineTokens = 4;      // combine item: 4 tokens
+constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroing item
+
+// control-block slots (int32 each)
+enum CtrlSlot : int {
+  C_MAGIC = 0, C_TICKET = 1, C_ZDONE = 2, C_LDONE = 3, C_KDONE = 4, C_PLAN = 5, C_SDONE = 6,
+  C_DDONE = 7, C_EXIT = 8, C_NMT = 9, C_ERR = 16, C_NSLOTS = 32
+};
+constexpr int kMagic = 0x4d6f4531;     // "MoE1"
+
+// which phases a launch runs
+enum PhaseBits : int { PH_ROUTE = 1, PH_PERMUTE = 2, PH_FFN = 4, PH_COMBINE = 8, PH_IDS_GIVEN = 16 };
+
+struct Tiles {
+  int mg;          // 16-row token groups per m-tile (1, 2, 4 or 8)
+  int bm;          // rows per m-tile = 16 * mg
+  int tk;          // tokens per top-k / scatter chunk (tk * k <= 256)
+};
+
+struct Layout {
+  Tiles tiles;
+  int64_t T;
+  int n_lt, n_le;        // router items: token tiles x expert blocks
+  int n_kc;              // top-k / scatter chunks
+  int mt_routed_max;     // bound on routed m-tiles
+  int n_shmt;            // shared-expert m-tiles
+  int nt_gu, nt_dn;      // gate/up and down items per m-tile
+  int n_comb;            // combine items
+  int n_zero;            // counter-clearing items
+  int64_t rows_h;        // rows of H and Y: T*k + n_shared*T
+  // byte offsets into the workspace
+  size_t off_gudone, off_logits, off_ids, off_wts, off_hist, off_counts, off_offsets, off_mtoff,
+      off_perm, off_invperm, off_h, off_y, total;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline size_t dtype_size(int dt) { return dt == MOE_F32 ? 4 : (dt == MOE_BF16 ? 2 : 1); }
+
+// Checks shapes and dtypes only (no pointers).
+inline moe_status validate_problem(const moe_problem *p) {
+  if (!p) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->T < 0 || p->d <= 0 || p->n <= 0 || p->E <= 0 || p->k <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->k > p->E) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->n_shared != 0 && p->n_shared != 1) return MOE_ERR_INVALID_ARGUMENT;
+  const int a = p->act_dtype, w = p->w_dtype;
+  if (a < 0 || a > 2 || w < 0 || w > 2) return MOE_ERR_INVALID_ARGUMENT;
+  const bool ok = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && w == MOE_BF16) ||
+                  (a == MOE_BF16 && w == MOE_FP8_E4M3);
+  if (!ok) return MOE_ERR_UNSUPPORTED;
+  if (w == MOE_FP8_E4M3) {
+    if (p->scale_block != 128) return MOE_ERR_UNSUPPORTED;
+  } else if (p->scale_block != 0) {
+    return MOE_ERR_INVALID_ARGUMENT;
+  }
+  if (p->E > kMaxE || p->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (p->d % 256 || p->n % 256) return MOE_ERR_UNSUPPORTED;
+  if (p->T * (int64_t)p->k >= (int64_t(1) << 31) - 1) return MOE_ERR_UNSUPPORTED;
+  if (p->T * (int64_t)(p->d > p->n ? p->d : p->n) >= (int64_t(1) << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+inline Tiles choose_tiles(const moe_problem *p) {
+  Tiles t;
+  const double mean_rows = p->E > 0 ? double(p->T) * p->k / p->E : 0.0;
+  t.mg = mean_rows <= 16 ? 1 : mean_rows <= 32 ? 2 : mean_rows <= 64 ? 4 : 8;
+  t.bm = 16 * t.mg;
+  t.tk = 256 / p->k;
+  if (t.tk < 1) t.tk = 1;
+  return t;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline Layout make_layout(const moe_problem *p) {
+  Layout L{};
+  L.tiles = choose_tiles(p);
+  const int64_t T = p->T, k = p->k, E = p->E, bm = L.tiles.bm;
+  L.T = T;
+  L.n_lt = (int)ceil_div(T, kLogitTokens);
+  L.n_le = (int)ceil_div(E, kLogitExperts);
+  L.n_kc = (int)ceil_div(T, L.tiles.tk);
+  const int64_t tk = T * k;
+  int64_t bound = tk / bm + (E < tk ? E : tk);
+  if (bound > tk) bound = tk;
+  L.mt_routed_max = (int)bound;
+  L.n_shmt = p->n_shared ? (int)ceil_div(T, bm) : 0;
+  L.nt_gu = p->n / kGuCols;
+  L.nt_dn = (int)ceil_div(p->d, kDnCols);
+  L.n_comb = (int)ceil_div(T, kCombineTokens);
+  L.n_zero = (int)ceil_div(L.mt_routed_max + L.n_shmt, kZeroPerItem);
+  L.rows_h = tk + (int64_t)p->n_shared * T;
+  const size_t asz = dtype_size(p->act_dtype);
+  size_t o = kCtrlBytes;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.off_gudone = take(sizeof(int32_t) * (size_t)(L.mt_routed_max + L.n_shmt + 1));
+  L.off_logits = take(sizeof(float) * (size_t)(T * E));
+  L.off_ids = take(sizeof(int32_t) * (size_t)tk);
+  L.off_wts = take(sizeof(float) * (size_t)tk);
+  L.off_hist = take(sizeof(int32_t) * (size_t)L.n_kc * (size_t)E);
+  L.off_counts = take(sizeof(int32_t) * (size_t)E);
+  L.off_offsets = take(sizeof(int32_t) * (size_t)(E + 1));
+  L.off_mtoff = take(sizeof(int32_t) * (size_t)(E + 1));
+  L.off_perm = take(sizeof(int32_t) * (size_t)tk);
+  L.off_invperm = take(sizeof(int32_t) * (size_t)tk);
+  L.off_h = take(asz * (size_t)L.rows_h * (size_t)p->n);
+  L.off_y = take(asz * (size_t)L.rows_h * (size_t)p->d);
+  L.total = o;
+  return L;
+}
+
+}  // namespace moe

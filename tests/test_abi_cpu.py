@@ -1,0 +1,115 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and its host-only entry points validate arguments.  No compute
+call is made (validation returns before anything is enqueued)."""
+import ctypes
+import os
+
+import pytest
+
+import routed_grouped_gemm_amd as moe
+
+INVALID, UNSUPPORTED, TOO_SMALL = 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        from routed_grouped_gemm_amd import build
+        build.build()
+    return moe.lib()
+
+
+def test_exports_every_header_function(L):
+    names = moe.header_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(L, name), f"libmoe.so does not export {name}"
+
+
+def test_version_and_strings(L):
+    assert moe.abi_version() == 1
+    for code, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARGUMENT"), (2, "MOE_ERR_UNSUPPORTED"),
+                       (3, "MOE_ERR_WORKSPACE_TOO_SMALL"), (4, "MOE_ERR_HIP"), (5, "MOE_ERR_DEVICE_FAULT")]:
+        assert moe.status_string(code) == name
+    assert moe.status_string(77) == "MOE_ERR_UNKNOWN"
+
+
+def ws_size(p):
+    out = ctypes.c_size_t(0)
+    return moe.lib().moe_workspace_size(ctypes.byref(p), ctypes.byref(out)), out.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=16, d=2048, n=512, E=256, k=8), 0),
+    (dict(T=0, d=2048, n=512, E=256, k=8), 0),
+    (dict(T=64, d=256, n=512, E=8, k=2, act="f32", w="f32"), 0),
+    (dict(T=4, d=7168, n=2048, E=256, k=8, n_shared=1, w="fp8"), 0),
+    (dict(T=16, d=2048, n=512, E=256, k=0), INVALID),
+    (dict(T=16, d=2048, n=512, E=4, k=5), INVALID),
+    (dict(T=-1, d=2048, n=512, E=8, k=2), INVALID),
+    (dict(T=16, d=2048, n=512, E=8, k=2, n_shared=2), INVALID),
+    (dict(T=16, d=2000, n=512, E=8, k=2), UNSUPPORTED),
+    (dict(T=16, d=2048, n=500, E=8, k=2), UNSUPPORTED),
+    (dict(T=16, d=2048, n=512, E=2048, k=2), UNSUPPORTED),
+    (dict(T=16, d=2048, n=512, E=8, k=2, act="f32", w="bf16"), UNSUPPORTED),
+    (dict(T=16, d=2048, n=512, E=8, k=2, act="f32", w="fp8"), UNSUPPORTED),
+])
+def test_workspace_size_validation(L, kw, code):
+    p = moe.problem(**kw)
+    rc, size = ws_size(p)
+    assert rc == code
+    if code == 0:
+        assert size >= 4096 and size % 256 == 0
+
+
+def test_workspace_size_monotone_in_T(L):
+    sizes = [ws_size(moe.problem(T, 2048, 512, 256, 8))[1] for T in (1, 16, 256, 4096)]
+    assert sizes == sorted(sizes)
+    # H and Y alone for T=4096: rows T*k, n and d bf16 columns
+    assert sizes[-1] > 4096 * 8 * (512 + 2048) * 2
+
+
+def test_scale_block_rules(L):
+    p = moe.problem(4, 256, 256, 4, 2, w="fp8")
+    p.scale_block = 64
+    assert ws_size(p)[0] == UNSUPPORTED
+    p = moe.problem(4, 256, 256, 4, 2)
+    p.scale_block = 128
+    assert ws_size(p)[0] == INVALID
+
+
+def test_compute_calls_reject_bad_arguments_before_launch(L):
+    """Host-side validation returns before any HIP call, so this runs without a GPU."""
+    p = moe.problem(16, 2048, 512, 256, 8)
+    W = moe.Weights()
+    VP = ctypes.c_void_p
+    fake = VP(1 << 20)  # never dereferenced: validation fails first
+    # null hidden
+    assert L.moe_forward(ctypes.byref(p), None, fake, None, ctypes.byref(W), fake, None, fake, 1 << 30, None) == INVALID
+    # null weights
+    assert L.moe_forward(ctypes.byref(p), fake, fake, None, ctypes.byref(W), VP(2 << 20), None, fake, 1 << 30, None) == INVALID
+    # misaligned hidden
+    assert L.moe_forward(ctypes.byref(p), VP((1 << 20) + 4), fake, None, ctypes.byref(W), fake, None, fake, 1 << 30, None) == INVALID
+    # out aliases hidden
+    W2 = moe.Weights(*([1 << 21] * 3 + [None] * 9))
+    assert L.moe_forward(ctypes.byref(p), fake, fake, None, ctypes.byref(W2), fake, None, fake, 1 << 30, None) == INVALID
+    # workspace too small (checked before any device query)
+    rc = L.moe_forward(ctypes.byref(p), fake, fake, None, ctypes.byref(W2), VP(3 << 20), None, fake, 4096, None)
+    assert rc == TOO_SMALL
+    # workspace misaligned
+    rc = L.moe_forward(ctypes.byref(p), fake, fake, None, ctypes.byref(W2), VP(3 << 20), None, VP((1 << 20) + 16), 1 << 30, None)
+    assert rc == INVALID
+    # fp8 without scales
+    p8 = moe.problem(4, 256, 256, 4, 2, w="fp8")
+    assert L.moe_forward(ctypes.byref(p8), fake, fake, None, ctypes.byref(W2), VP(3 << 20), None, fake, 1 << 30, None) == INVALID
+    # shared expert requested but missing
+    ps = moe.problem(4, 256, 256, 4, 2, n_shared=1)
+    assert L.moe_forward(ctypes.byref(ps), fake, fake, None, ctypes.byref(W2), VP(3 << 20), None, fake, 1 << 30, None) == INVALID
+    # route/permute argument checks
+    assert L.moe_route(ctypes.byref(p), fake, fake, None, None, fake, None, fake, 1 << 30, None) == INVALID
+    assert L.moe_permute(ctypes.byref(p), fake, None, fake, fake, fake, fake, 1 << 30, None) == INVALID
+    bad = moe.problem(16, 2048, 512, 4, 8)
+    assert L.moe_route(ctypes.byref(bad), fake, fake, None, fake, fake, None, fake, 1 << 30, None) == INVALID
+    # workspace init argument checks
+    assert L.moe_workspace_init(None, 1 << 20, None) == INVALID
+    assert L.moe_workspace_init(fake, 100, None) == INVALID

@@ -1,0 +1,226 @@
+"""GPU parity of the library against the CPU oracle, through the C ABI.
+
+Routing and permutation indices must match exactly; outputs must be within the
+relative Frobenius bound of their weight dtype (fp32 1e-5, bf16 2e-2, fp8 5e-2),
+over the whole output and for every token.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_grouped_gemm_amd as moe
+import synth
+from devinputs import out_to_f64, tensor, to_device
+from gpu_common import (TOL, check_permutation, check_routing, compare_outputs, full_parity, require_gpu,
+                        run_forward)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+_cache = {}
+
+
+def cfg_inputs(name, T=None):
+    key = (name, T)
+    if key not in _cache:
+        _cache[key] = synth.make_inputs(synth.config(name, T))
+    return _cache[key]
+
+
+# -- the named workloads ------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_fp32", "decode_bf16", "prefill_bf16", "skewed_bf16"])
+def test_forward_named_config(name):
+    print(f"[forward parity] {name}", flush=True)
+    res = full_parity(cfg_inputs(name))
+    print(f"  rel_frob={res['err']:.3e} worst_token={res['worst']:.3e} near_tie_flips={res['near_tie_flips']}")
+
+
+# -- small ragged workloads the oracle runs in full ----------------------------------
+ADHOC = [
+    # seed, T, d, n, E, k, act, w, shared, bias
+    (11, 37, 512, 768, 12, 3, "bf16", "bf16", 0, True),
+    (12, 45, 512, 256, 10, 4, "bf16", "fp8", 1, False),
+    (13, 23, 256, 256, 5, 5, "f32", "f32", 0, False),      # k = E
+    (14, 130, 256, 512, 6, 2, "f32", "f32", 1, True),      # several m-tiles per expert
+    (15, 300, 768, 512, 16, 4, "bf16", "bf16", 1, False),  # mean 75 rows/expert -> 128-row tiles
+    (16, 1, 512, 256, 7, 2, "bf16", "fp8", 0, True),       # T = 1
+    (17, 9, 256, 256, 1, 1, "bf16", "bf16", 0, False),     # E = 1, k = 1
+    (18, 200, 1024, 512, 64, 6, "bf16", "fp8", 1, True),   # ~19 rows/expert -> 32-row tiles
+    (19, 160, 512, 256, 8, 2, "bf16", "bf16", 0, False),   # ~40 rows/expert -> 64-row tiles
+]
+
+
+@pytest.mark.parametrize("case", ADHOC, ids=lambda c: f"seed{c[0]}_T{c[1]}_E{c[4]}k{c[5]}_{c[7]}_sh{c[8]}")
+def test_forward_adhoc(case):
+    seed, T, d, n, E, k, act, w, shared, bias = case
+    print(f"[forward parity] adhoc {case}", flush=True)
+    inp = synth.make_tiny(seed, T, d, n, E, k, act=act, w=w, shared=shared, bias=bias)
+    res = full_parity(inp)
+    print(f"  rel_frob={res['err']:.3e} worst_token={res['worst']:.3e}")
+
+
+# -- routing alone -------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_fp32", "decode_bf16", "prefill_bf16", "skewed_bf16"])
+def test_route_alone(name):
+    inp = cfg_inputs(name)
+    c = inp.cfg
+    p, x, wr, b, W = to_device(inp)
+    ws = moe.alloc_workspace(p)
+    ids, wts, logits = moe.route(p, x, wr, b, ws, want_logits=True)
+    torch.cuda.synchronize()
+    assert moe.last_device_error(ws) == 0
+    r = dict(topk_ids=ids, topk_weights=wts, logits=logits)
+    check_routing(oracle.InputsView(inp), r, c["k"], c["E"])
+    # the forward pass routes identically
+    _, r2, _ = run_forward(inp)
+    assert torch.equal(r2["topk_ids"], ids) and torch.equal(r2["topk_weights"], wts)
+    assert torch.equal(r2["logits"], logits)
+
+
+# -- permutation alone ---------------------------------------------------------------
+def _permute_case(T, E, k, seed, mode):
+    rng = np.random.default_rng(seed)
+    if mode == "random":
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    elif mode == "hot":  # expert 3 in every token
+        ids = np.stack([np.concatenate([[3], [e for e in rng.permutation(E) if e != 3][:k - 1]]) for _ in range(T)])
+    elif mode == "few":  # only experts 0..k used -> most experts empty
+        ids = np.stack([rng.permutation(k + 1)[:k] for _ in range(T)])
+    return ids.astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k,mode", [(1, 8, 2, "random"), (16, 256, 8, "random"), (4096, 256, 8, "random"),
+                                        (2048, 64, 4, "hot"), (333, 128, 6, "few"), (77, 5, 5, "random"),
+                                        (1000, 1024, 1, "random"), (64, 300, 256, "random")])
+def test_permute_exact(T, E, k, mode):
+    ids = _permute_case(T, E, k, T + E + k, mode)
+    p = moe.problem(T, 256, 256, E, k)
+    ws = moe.alloc_workspace(p)
+    counts, offsets, perm, inv = moe.permute(p, torch.from_numpy(ids).cuda(), ws)
+    torch.cuda.synchronize()
+    assert moe.last_device_error(ws) == 0
+    rc, ro, rp, ri = oracle.permute(ids, E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(perm.cpu().numpy(), rp)
+    assert np.array_equal(inv.cpu().numpy(), ri)
+
+
+# -- determinism -----------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["decode_bf16", "skewed_bf16"])
+def test_bitwise_determinism_across_grids_and_schedules(name):
+    inp = cfg_inputs(name)
+    out0, r0, ctx = run_forward(inp)
+    p, x, wr, b, W, ws = (ctx[k] for k in ("p", "x", "wr", "b", "W", "ws"))
+    outs = []
+    for _ in range(3):
+        outs.append(moe.forward(p, x, wr, b, W, ws))
+    for g in (1, 7, 64, 300):
+        outs.append(moe.forward(p, x, wr, b, W, ws, grid_wgs=g))
+    outs.append(moe.forward(p, x, wr, b, W, ws, schedule=1))
+    outs.append(moe.forward(p, x, wr, b, W, ws, schedule=1, grid_wgs=5))
+    torch.cuda.synchronize()
+    assert moe.last_device_error(ws) == 0
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), out0.view(torch.int16))
+
+
+# -- edge cases ------------------------------------------------------------------------
+def test_zero_hidden_gives_zero_and_lowest_ids():
+    inp = synth.make_tiny(21, 20, 512, 256, 9, 3, act="bf16", w="bf16")
+    inp.hidden = np.zeros_like(inp.hidden)
+    out, r, _ = run_forward(inp)
+    assert torch.count_nonzero(out.float()) == 0
+    assert np.array_equal(r["topk_ids"].cpu().numpy(), np.tile(np.arange(3), (20, 1)))
+    assert np.allclose(r["topk_weights"].cpu().numpy(), 1.0 / 3, rtol=1e-6)
+
+
+def test_duplicated_router_rows_tie_to_lower_id():
+    inp = synth.make_tiny(22, 64, 256, 256, 6, 4, act="bf16", w="bf16")
+    inp.w_router[4] = inp.w_router[1]
+    inp.w_router[5] = inp.w_router[0]
+    res = full_parity(inp)
+    ids = res["r"]["topk_ids"].cpu().numpy()
+    for t in range(64):
+        row = list(ids[t])
+        for lo, hi in ((1, 4), (0, 5)):
+            if lo in row and hi in row:
+                assert row.index(lo) < row.index(hi)
+            assert not (hi in row and lo not in row), "tied expert kept without its lower-id twin"
+
+
+def test_empty_batch_is_a_no_op():
+    inp = synth.make_tiny(23, 4, 256, 256, 4, 2, act="bf16", w="bf16")
+    p, x, wr, b, W = to_device(inp)
+    p0 = moe.problem(0, 256, 256, 4, 2)
+    ws = moe.alloc_workspace(p)
+    out = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    moe.forward(p0, x, wr, b, W, ws, out=out)
+    torch.cuda.synchronize()
+    assert moe.last_device_error(ws) == 0
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace, sized for the largest call, serves calls of other shapes in turn."""
+    big = synth.make_tiny(24, 300, 512, 512, 16, 4, act="bf16", w="bf16")
+    p_big, *_ = to_device(big)
+    ws = moe.alloc_workspace(p_big)
+    for T in (300, 7, 130, 1, 300):
+        inp = synth.make_tiny(24, T, 512, 512, 16, 4, act="bf16", w="bf16")
+        p, x, wr, b, W = to_device(inp)
+        out, r = moe.forward(p, x, wr, b, W, ws, route_out=True)
+        torch.cuda.synchronize()
+        assert moe.last_device_error(ws) == 0
+        v = oracle.InputsView(inp)
+        L, ids, gids, mism = check_routing(v, r, 4, 16)
+        ref = oracle.moe_forward_view(v)[0]
+        assert not mism.any()
+        compare_outputs(out_to_f64(out), ref, TOL["bf16"], f"reuse T={T}")
+
+
+def test_uninitialised_workspace_is_reported_not_hung():
+    inp = synth.make_tiny(25, 8, 256, 256, 4, 2, act="bf16", w="bf16")
+    p, x, wr, b, W = to_device(inp)
+    nbytes = moe.workspace_size(p)
+    ws = torch.zeros(nbytes + 256, dtype=torch.uint8, device="cuda")
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + nbytes]
+    moe.forward(p, x, wr, b, W, ws)
+    torch.cuda.synchronize()
+    assert moe.last_device_error(ws) == 5
+    moe.workspace_init(ws)
+    moe.forward(p, x, wr, b, W, ws)
+    assert moe.last_device_error(ws) == 0
+
+
+# -- graph capture -----------------------------------------------------------------------
+def test_hip_graph_replay_matches_eager():
+    inp = cfg_inputs("decode_bf16")
+    out0, r0, ctx = run_forward(inp)
+    p, x, wr, b, W, ws = (ctx[k] for k in ("p", "x", "wr", "b", "W", "ws"))
+    out = torch.empty_like(out0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.forward(p, x, wr, b, W, ws, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(p, x, wr, b, W, ws, out=out)
+    for rep in range(5):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert moe.last_device_error(ws) == 0
+        assert torch.equal(out.view(torch.int16), out0.view(torch.int16)), f"replay {rep} differs"
+        eager = moe.forward(p, x, wr, b, W, ws)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(eager.view(torch.int16), out0.view(torch.int16))

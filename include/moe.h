@@ -110,6 +110,11 @@ typedef struct {
 
 /* (host) optional launch controls, for tests and ablations; pass NULL for the defaults.
  * grid_wgs: workgroups of the persistent launch (0 = CUs x occupancy).
+ * trace/trace_bytes: optional device buffer of 32-byte records, one per work item, indexed
+ *           by ticket: {start, end} of the 100 MHz device clock (uint64 each), the ticket
+ *           (int64) and (workgroup << 32 | item kind) (int64); kinds: 0 clear, 1 router,
+ *           2 top-k (+ plan), 3 shared gate/up, 4 scatter, 5 gate/up, 6 down, 7 combine.
+ *           Items beyond the buffer are not recorded.  NULL (default) records nothing.
  * schedule: 0 = dynamic (work items taken from an atomic queue in the workspace),
  *           1 = static (item i is bound to workgroup i mod grid, like static expert-to-SM
  *               binding in the Weave review, section 4.2),
@@ -119,7 +124,9 @@ typedef struct {
 typedef struct {
   int32_t grid_wgs;
   int32_t schedule;
-  int32_t reserved[6];
+  void *trace;
+  int64_t trace_bytes;
+  int32_t reserved[4];
 } moe_launch_options;
 
 /* Bytes of workspace a problem needs (host only, no HIP call).  The bound depends on T*k
@@ -128,7 +135,7 @@ typedef struct {
 moe_status moe_workspace_size(const moe_problem *p, size_t *bytes /* (host) out */);
 
 /* Clears the workspace's control block (a fill kernel on `stream`).  Call once after
- * allocating a workspace, and again after a MOE_ERR_DEVICE_FAULT.  Needs at least 4096
+ * allocating a workspace, and again after a MOE_ERR_DEVICE_FAULT.  Needs at least 65536
  * bytes. */
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 

@@ -58,7 +58,8 @@ class RouteOut(ctypes.Structure):
 
 
 class LaunchOptions(ctypes.Structure):
-    _fields_ = [("grid_wgs", ctypes.c_int32), ("schedule", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
+    _fields_ = [("grid_wgs", ctypes.c_int32), ("schedule", ctypes.c_int32), ("trace", ctypes.c_void_p),
+                ("trace_bytes", ctypes.c_int64), ("reserved", ctypes.c_int32 * 4)]
 
 
 _lib = None
@@ -192,9 +193,11 @@ def make_weights(weights: dict) -> Weights:
 
 
 def forward(p: Problem, hidden, w_router, bias, weights, ws, out=None, route_out=False, grid_wgs=0,
-            schedule=0):
+            schedule=0, trace=None):
     """The whole layer.  weights: dict with w_gate, w_up, w_down (+ s_*, sh_*) device tensors,
-    or a prebuilt Weights struct.  Returns out, or (out, dict of routing tensors)."""
+    or a prebuilt Weights struct.  trace: optional device tensor receiving one 32-byte record
+    per work item (see moe_launch_options in include/moe.h).  Returns out, or (out, dict of
+    routing tensors)."""
     dev = hidden.device
     T, k, E, d = p.T, p.k, p.E, p.d
     if out is None:
@@ -213,8 +216,9 @@ def forward(p: Problem, hidden, w_router, bias, weights, ws, out=None, route_out
         ro = RouteOut(*[_ptr(rdict[f[0]]) for f in RouteOut._fields_])
     wp, wb = _ws(ws)
     L = _load()
-    if grid_wgs or schedule:
-        opts = LaunchOptions(int(grid_wgs), int(schedule))
+    if grid_wgs or schedule or trace is not None:
+        opts = LaunchOptions(int(grid_wgs), int(schedule), _ptr(trace),
+                             0 if trace is None else trace.numel() * trace.element_size())
         code = L.moe_forward_ex(ctypes.byref(p), _ptr(hidden), _ptr(w_router), _ptr(bias), ctypes.byref(W),
                                 _ptr(out), ctypes.byref(ro) if ro is not None else None, wp, wb, _stream(),
                                 ctypes.byref(opts))

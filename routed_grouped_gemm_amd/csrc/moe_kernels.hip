@@ -6,29 +6,30 @@
 // explainer, section 四), in this order:
 //
 //   Z  clear the per-m-tile dependency counters
-//   L  router logits: 16 tokens x 64 experts per item (MFMA)
+//   L  router logits: 16 tokens x 16 experts per item, K split over the 4 waves (MFMA)
 //   K  top-k + softmax over the kept logits for a chunk of tokens, and the chunk's
 //      per-expert histogram; the last K item to finish builds the plan (scan of the
-//      histograms, expert offsets, m-tile offsets)
+//      histograms, expert offsets, the m-tile descriptor table)
 //   SG shared-expert gate/up items (need no routing, so they overlap the plan)
 //   S  stable scatter of a chunk: perm / inv_perm
-//   G  gate/up items (expert, m-tile, 64 H columns): gathered token rows x W_gate/W_up,
-//      SwiGLU in registers, H written once
-//   D  down items (m-tile, 128 output columns): H rows x W_down -> Y
+//   G  gate/up items (m-tile, H columns): gathered token rows x W_gate/W_up, SwiGLU in
+//      registers, H written once
+//   D  down items (m-tile, output columns): H rows x W_down -> Y
 //   C  combine items: out[t] = sum_j w[t,j] * Y[inv_perm[t*k+j]] (+ Y_shared[t]), fixed
 //      slot order, float32, one rounding, no float atomics
 //
 // A work item only ever waits for items with smaller tickets.  Those were taken by
-// workgroups that are running, so every wait ends whatever the grid size or how many
-// workgroups are resident.  Every wait is also bounded in time; a timeout sets a fault
-// flag that makes every later wait give up, so the kernel always exits.
+// workgroups that are running (a workgroup holds at most its current ticket and the next
+// one it prefetched, which is larger), so every wait ends whatever the grid size or how
+// many workgroups are resident.  Every wait is also bounded in time; a timeout sets a
+// fault flag that makes every later wait give up, so the kernel always exits.
 //
 // Expert tiles: weights are the MFMA A operand (rows = output channels, K contiguous, one
 // 16-byte load per lane straight from HBM into registers, double-buffered), token rows
-// are the B operand (gathered rows staged through LDS with an XOR swizzle).  This is the
-// operand-swapped form that suits small M (GC-MoE article, "two MMA implementations"):
-// the weight stream, the HBM-bound part, is read exactly once per item and never
-// passes through LDS.
+// are the B operand (gathered rows copied global -> LDS by the load-to-LDS path, with an
+// XOR swizzle, double-buffered).  This is the operand-swapped form that suits small M
+// (GC-MoE article, "two MMA implementations"): the weight stream, the HBM-bound part, is
+// read exactly once per item and never passes through LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -44,23 +45,28 @@ using namespace moe;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 enum : int { WF32 = 0, WBF16 = 1, WFP8 = 2 };
 
-// K elements per 16-byte lane load (KU), loads per chunk (FL), chunk (KC = FL*KU):
-// every chunk stages 512 bytes of each activation row.
-template <int WT> struct WTr;
-template <> struct WTr<WF32> { static constexpr int FL = 8, KU = 16, KC = 128, WSZ = 4, ASZ = 4; };
-template <> struct WTr<WBF16> { static constexpr int FL = 8, KU = 32, KC = 256, WSZ = 2, ASZ = 2; };
-template <> struct WTr<WFP8> { static constexpr int FL = 4, KU = 64, KC = 256, WSZ = 1, ASZ = 2; };
-constexpr int kRowChunkBytes = 512;
+// KU: K elements per 16-byte weight load of one lane; WSZ/ASZ: weight/activation bytes
+template <int WT> struct Ty;
+template <> struct Ty<WF32> { static constexpr int KU = 16, WSZ = 4, ASZ = 4; };
+template <> struct Ty<WBF16> { static constexpr int KU = 32, WSZ = 2, ASZ = 2; };
+template <> struct Ty<WFP8> { static constexpr int KU = 64, WSZ = 1, ASZ = 2; };
+
+// per-kernel tile shape: MG 16-token groups per m-tile, NF weight fragments per wave,
+// FL 16-byte weight loads per fragment per K chunk
+template <int WT, int MG> struct Shape {
+  static constexpr int NF = MG == 1 ? 2 : 4;
+  static constexpr int FL = WT == WFP8 ? (MG == 1 ? 4 : 2) : (MG == 1 ? 8 : 4);
+};
 
 struct KParams {
   int T, d, n, E, k, S;
   int phases;
-  int bm, tk;
+  int bm, tk, gu_cols, dn_cols;
   int n_lt, n_le, n_kc, n_shmt, nt_gu, nt_dn, n_comb, n_zero, mt_cap;
-  int n_static;  // Z + L + K + SG + S tickets
   int schedule;  // 0 dynamic, 1 static
   const void *x, *wr;
   const float *bias;
@@ -74,34 +80,89 @@ struct KParams {
   float *wts;
   int *counts, *offsets, *perm, *inv_perm;
   int *ctrl, *gudone, *hist, *mtoff;
+  int4 *desc;
   void *H, *Y;
+  unsigned long long *trace;
+  long long trace_cap;
 };
 
 // ---------------------------------------------------------------------------------
-// scoped atomics and bounded waits
+// small helpers
 // ---------------------------------------------------------------------------------
-__device__ __forceinline__ int ld_acquire(const int *p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// otid() behind an empty volatile asm: values derived from it are recomputed in each
+// work item instead of being hoisted out of the persistent loop (where they would stay
+// live, in registers, across every item)
+__device__ __forceinline__ int otid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
 }
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 16 bytes per lane, global -> LDS; lane l lands at lds_base + 16*l (lds_base uniform).
+// COH selects the device-coherent cache policy (SC1) for data written in this launch.
+template <bool COH>
+__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                   (__attribute__((address_space(3))) void *)lds_base, 16, 0, COH ? 16 : 0);
+}
+
 __device__ __forceinline__ int ld_relaxed(const int *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int add_acq_rel(int *p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+
+// Data that one workgroup writes and another reads during the same launch moves through
+// device-coherent accesses (agent-scope relaxed atomics: stores write through to the
+// device coherence point, loads never hit a stale line of another XCD's L2).  A producer
+// then only waits for its stores to complete (s_waitcnt) before bumping a counter, and a
+// consumer reads after seeing the counter: no agent-scope fence, so no whole-L2 write-back
+// or invalidation on the hot path (those cost more than the work items themselves).
+__device__ __forceinline__ void st_coh(int *p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void st_coh(float *p, float v) {
+  __hip_atomic_store(reinterpret_cast<int *>(p), __float_as_int(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_release(int *p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_coh64(void *p, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_coh(const int *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ float ld_coh(const float *p) {
+  return __int_as_float(__hip_atomic_load(reinterpret_cast<const int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ uint64_t ld_coh64(const void *p) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int4 ld_coh_int4(const int4 *p) {
+  const uint64_t a = ld_coh64(p), b = ld_coh64(reinterpret_cast<const char *>(p) + 8);
+  return make_int4((int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)(uint32_t)b, (int)(uint32_t)(b >> 32));
+}
+__device__ __forceinline__ uint4 ld_coh16(const void *p) {
+  const uint64_t a = ld_coh64(p), b = ld_coh64(reinterpret_cast<const char *>(p) + 8);
+  return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+}
+__device__ __forceinline__ void st_coh_int4(int4 *p, int4 v) {
+  st_coh64(p, (uint64_t)(uint32_t)v.x | ((uint64_t)(uint32_t)v.y << 32));
+  st_coh64(reinterpret_cast<char *>(p) + 8, (uint64_t)(uint32_t)v.z | ((uint64_t)(uint32_t)v.w << 32));
 }
 
 constexpr uint64_t kSpinTicks = 200000000ull;  // ~2 s of the 100 MHz wall clock
 
 // Thread 0 only: wait until *p >= target.  False on timeout or an earlier fault.
+// Polls with relaxed agent-scope loads (an acquire load would invalidate caches on every
+// poll); the caller issues one acquire fence after the wait succeeds.  Polls back off
+// from ~0.1 us to ~0.9 us apart: hundreds of waiting workgroups polling one address at full
+// rate would saturate that address's memory channel and slow every other load.
 __device__ bool spin_geq(const int *p, int target, int *err) {
-  if (ld_acquire(p) >= target) return true;
+  if (ld_relaxed(p) >= target) return true;
   const uint64_t t0 = wall_clock64();
-  for (;;) {
-    __builtin_amdgcn_s_sleep(2);
-    if (ld_acquire(p) >= target) return true;
+  for (int it = 0;; ++it) {
+    if (it < 8) __builtin_amdgcn_s_sleep(4);
+    else if (it < 32) __builtin_amdgcn_s_sleep(12);
+    else __builtin_amdgcn_s_sleep(32);
+    if (ld_relaxed(p) >= target) return true;
     if (ld_relaxed(err) != 0) return false;
     if (wall_clock64() - t0 > kSpinTicks) {
       __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -110,39 +171,17 @@ __device__ bool spin_geq(const int *p, int target, int *err) {
   }
 }
 
-// ---------------------------------------------------------------------------------
-// shared memory
-// ---------------------------------------------------------------------------------
-template <int MG> struct Smem {
-  union {
-    struct {
-      char act[2][MG * 16 * kRowChunkBytes];
-    } g;
-    struct {
-      int ids[256];
-      float wl[kWaves][kMaxK];
-      int hist[kMaxE];
-      int tmp[kMaxE];
-    } r;
-  } u;
-  int rows[MG * 16];
-  int bcast[4];
-};
-
-// ---------------------------------------------------------------------------------
-// numeric helpers
-// ---------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
-  // exact for values with <= 8 significant bits (fp8 values)
+  // exact for values with <= 8 significant bits (decoded fp8 values)
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
 }
 
 // 8 OCP e4m3 codes -> 8 bf16 (exact)
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t a, uint32_t b) {
-  f2v p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)a, false);
-  f2v p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)a, true);
-  f2v p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);
-  f2v p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, true);
+  const f2v p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)a, false);
+  const f2v p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)a, true);
+  const f2v p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);
+  const f2v p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, true);
   uint4 r;
   r.x = pack_hi16(p0.x, p0.y);
   r.y = pack_hi16(p1.x, p1.y);
@@ -152,122 +191,128 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t a, uint32_t b) {
 }
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
-}
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
-}
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// monotone map float -> uint32 (after -0.0 -> +0.0), larger float -> larger key
+// monotone map float -> uint32 (after -0.0 -> +0.0): larger float -> larger key
 __device__ __forceinline__ uint32_t ordered_key(float v) {
   v = v + 0.0f;  // -0.0 + 0.0 = +0.0 under round-to-nearest
   const uint32_t u = __float_as_uint(v);
   return (u & 0x80000000u) ? ~u : (u ^ 0x80000000u);
 }
 __device__ __forceinline__ float key_value(uint32_t k) {
-  const uint32_t u = (k & 0x80000000u) ? (k ^ 0x80000000u) : ~k;
-  return __uint_as_float(u);
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+// one MFMA step: acc += W(16 rows x KU) . A(16 tokens x KU)^T over this lane's K slice
+template <int WT>
+__device__ __forceinline__ f4 mfma_step(const uint4 &w, const uint4 &a0, const uint4 &a1, f4 acc) {
+  if constexpr (WT == WBF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, a0),
+                                                   acc, 0, 0, 0);
+  } else if constexpr (WT == WF32) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.x), __uint_as_float(a0.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.y), __uint_as_float(a0.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.z), __uint_as_float(a0.z), acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.w), __uint_as_float(a0.w), acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w.x, w.y), __builtin_bit_cast(bf16x8, a0), acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w.z, w.w), __builtin_bit_cast(bf16x8, a1), acc, 0, 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------------
-// MFMA tile core: acc[NF][MG] (+)= W[NF frags of 16 rows, K] . A[MG groups of 16 rows, K]^T
+// expert tile core: acc[NF][MG] = W[NF frags of 16 rows, K] . A[MG groups of 16 rows, K]^T
 //
-// lane l = 16*g + j: holds weight row (frag base + j), K bytes [64*f + 16*g, +16) of
-// every 64-byte step f; the activation operand of token (mg*16 + j) over the same K
-// positions; result D[4*g + r][j] = channel (frag base + 4*g + r), token (mg*16 + j).
+// lane l = 16*g + j holds weight row (frag base + j), bytes [64*f + 16*g, +16) of every
+// 64-byte step f of the row, and the activation operand of token (16*mg + j) over the
+// same K positions; result D[4*g + r][j] = channel (frag base + 4*g + r), token 16*mg + j.
 // ---------------------------------------------------------------------------------
-template <int WT, int NF, int MG> struct Gemm {
-  using Tr = WTr<WT>;
-  static constexpr int FL = Tr::FL;
+template <int WT, int MG> struct Core {
+  static constexpr int NF = Shape<WT, MG>::NF, FL = Shape<WT, MG>::FL;
+  static constexpr int KU = Ty<WT>::KU, ASZ = Ty<WT>::ASZ;
+  static constexpr int KC = FL * KU;            // K per chunk
+  static constexpr int RB = KC * ASZ;           // activation bytes per row per chunk
+  static constexpr int NCOL = RB / 16;          // 16-byte columns per row
   static constexpr int BMR = MG * 16;
-  static constexpr int STG = BMR * (kRowChunkBytes / 16) / kThreads;  // uint4 per thread
+  static constexpr int RPK = 1024 / RB;         // rows per 1 KB load-to-LDS block
+  static constexpr int NDMA = BMR * RB / 1024 / kWaves;
+  static constexpr int BUF = BMR * RB;          // bytes of one LDS buffer
+  static_assert(NDMA >= 1 && RPK >= 1, "tile shape");
 
-  // wrow[f]: this lane's weight row start (+16*g already added); sc[f]: fp8 scale row of
-  // the frag's 128-row block (nullptr otherwise); arow: activation matrix, `rows` LDS
-  // list of its row indices (valid, clamped); kbytes_a: bytes per activation row.
-  __device__ static void run(f4 (&acc)[NF][MG], const char *const (&wrow)[NF],
-                             const float *const (&sc)[NF], const char *arow, size_t kbytes_a,
-                             const int *rows, char (*act)[BMR * kRowChunkBytes], int K, int ngroups) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, g = lane >> 4, j = lane & 15;
-    const int nch = K / Tr::KC;
+  // COH: the activation rows were written earlier in this launch (H), so they are read
+  // with the device-coherent policy
+  template <bool COH>
+  __device__ static void run(f4 (&acc)[NF][MG], const char *const (&wrow)[NF], const float *const (&sc)[NF],
+                             const char *abase, size_t arow_bytes, const int *rows, char *lds, int K, int ngroups) {
+    const int tid = otid(), lane = tid & 63, g = lane >> 4, j = lane & 15;
+    const int wv = uni(tid >> 6);
+    const int nch = K / KC;
 #pragma unroll
     for (int a = 0; a < NF; ++a)
 #pragma unroll
       for (int b = 0; b < MG; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
-    uint4 wA[NF][FL], wB[NF][FL];
-    uint4 st[STG];
-    const int nk128 = K / 128;
-
-    auto load_w = [&](uint4(&W)[NF][FL], int c) {
+    const char *asrc[NDMA];
+#pragma unroll
+    for (int s = 0; s < NDMA; ++s) {
+      const int q = s * kWaves + wv;
+      const int r = q * RPK + lane / NCOL;
+      const int col = (lane % NCOL) ^ (r & (NCOL - 1));
+      asrc[s] = abase + (size_t)rows[r] * arow_bytes + col * 16;
+    }
+    auto dma = [&](int c, int buf) {
+#pragma unroll
+      for (int s = 0; s < NDMA; ++s) dma16<COH>(asrc[s] + (size_t)c * RB, lds + buf * BUF + (s * kWaves + wv) * 1024);
+    };
+    auto ldw = [&](uint4(&W)[NF][FL], int c) {
 #pragma unroll
       for (int f = 0; f < FL; ++f)
 #pragma unroll
         for (int a = 0; a < NF; ++a)
-          W[a][f] = *reinterpret_cast<const uint4 *>(wrow[a] + (size_t)c * (FL * 64) + f * 64);
-    };
-    auto load_a = [&](int c) {
-#pragma unroll
-      for (int s = 0; s < STG; ++s) {
-        const int idx = tid + kThreads * s;
-        const int r = idx >> 5, col = idx & 31;
-        st[s] = *reinterpret_cast<const uint4 *>(arow + (size_t)rows[r] * kbytes_a +
-                                                 (size_t)c * kRowChunkBytes + col * 16);
-      }
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-      for (int s = 0; s < STG; ++s) {
-        const int idx = tid + kThreads * s;
-        const int r = idx >> 5, col = idx & 31;
-        *reinterpret_cast<uint4 *>(act[buf] + r * kRowChunkBytes + ((col ^ (r & 31)) << 4)) = st[s];
-      }
+          W[a][f] = __builtin_bit_cast(
+              uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow[a] + (size_t)c * (FL * 64) + f * 64)));
     };
     auto compute = [&](const uint4(&W)[NF][FL], int buf, int c) {
-      const char *A = act[buf];
+      const char *A = lds + buf * BUF;
       if constexpr (WT == WFP8) {
-        float s0[NF], s1[NF];
+        constexpr int BPC = FL / 2;             // 128-wide scale blocks per chunk
+        constexpr int MGC = MG < 4 ? MG : 4;    // token groups per partial-sum pass
 #pragma unroll
-        for (int a = 0; a < NF; ++a) {
-          s0[a] = sc[a][2 * c];
-          s1[a] = (2 * c + 1 < nk128) ? sc[a][2 * c + 1] : 0.f;
-        }
+        for (int blk = 0; blk < BPC; ++blk) {
+          float s[NF];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          f4 tmp[NF][MG];
+          for (int a = 0; a < NF; ++a) s[a] = sc[a][c * BPC + blk];
 #pragma unroll
-          for (int a = 0; a < NF; ++a)
+          for (int b0 = 0; b0 < MG; b0 += MGC) {
+            if (b0 < ngroups) {
+              f4 tmp[NF][MGC];
 #pragma unroll
-            for (int b = 0; b < MG; ++b) tmp[a][b] = f4{0.f, 0.f, 0.f, 0.f};
+              for (int a = 0; a < NF; ++a)
 #pragma unroll
-          for (int ff = 0; ff < 2; ++ff) {
-            const int f = blk * 2 + ff;
+                for (int b = 0; b < MGC; ++b) tmp[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int b = 0; b < MG; ++b) {
-              if (b < ngroups) {
-                const int r = b * 16 + j;
-                const int c0 = f * 8 + 2 * g;
-                const uint4 a0 = *reinterpret_cast<const uint4 *>(A + r * kRowChunkBytes + ((c0 ^ (r & 31)) << 4));
-                const uint4 a1 = *reinterpret_cast<const uint4 *>(A + r * kRowChunkBytes + (((c0 + 1) ^ (r & 31)) << 4));
-                const bf16x8 b0 = __builtin_bit_cast(bf16x8, a0);
-                const bf16x8 b1 = __builtin_bit_cast(bf16x8, a1);
+              for (int ff = 0; ff < 2; ++ff) {
+                const int f = blk * 2 + ff;
 #pragma unroll
-                for (int a = 0; a < NF; ++a) {
-                  const uint4 w = W[a][f];
-                  tmp[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w.x, w.y), b0, tmp[a][b], 0, 0, 0);
-                  tmp[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w.z, w.w), b1, tmp[a][b], 0, 0, 0);
+                for (int b = 0; b < MGC; ++b) {
+                  if (b0 + b < ngroups) {
+                    const int r = (b0 + b) * 16 + j;
+                    const int c0 = f * 8 + 2 * g;
+                    const uint4 a0 = *reinterpret_cast<const uint4 *>(A + r * RB + ((c0 ^ (r & (NCOL - 1))) << 4));
+                    const uint4 a1 =
+                        *reinterpret_cast<const uint4 *>(A + r * RB + (((c0 + 1) ^ (r & (NCOL - 1))) << 4));
+#pragma unroll
+                    for (int a = 0; a < NF; ++a) tmp[a][b] = mfma_step<WT>(W[a][f], a0, a1, tmp[a][b]);
+                  }
                 }
               }
+#pragma unroll
+              for (int a = 0; a < NF; ++a)
+#pragma unroll
+                for (int b = 0; b < MGC; ++b) acc[a][b0 + b] += tmp[a][b] * s[a];
             }
-          }
-#pragma unroll
-          for (int a = 0; a < NF; ++a) {
-            const float s = blk == 0 ? s0[a] : s1[a];
-#pragma unroll
-            for (int b = 0; b < MG; ++b) acc[a][b] += tmp[a][b] * s;
           }
         }
       } else {
@@ -278,115 +323,132 @@ template <int WT, int NF, int MG> struct Gemm {
             if (b < ngroups) {
               const int r = b * 16 + j;
               const int c0 = f * 4 + g;
-              const uint4 av = *reinterpret_cast<const uint4 *>(A + r * kRowChunkBytes + ((c0 ^ (r & 31)) << 4));
+              const uint4 av = *reinterpret_cast<const uint4 *>(A + r * RB + ((c0 ^ (r & (NCOL - 1))) << 4));
 #pragma unroll
-              for (int a = 0; a < NF; ++a) {
-                const uint4 w = W[a][f];
-                if constexpr (WT == WBF16) {
-                  acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                      __builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, av), acc[a][b], 0, 0, 0);
-                } else {
-                  acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.x), __uint_as_float(av.x), acc[a][b], 0, 0, 0);
-                  acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.y), __uint_as_float(av.y), acc[a][b], 0, 0, 0);
-                  acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.z), __uint_as_float(av.z), acc[a][b], 0, 0, 0);
-                  acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w.w), __uint_as_float(av.w), acc[a][b], 0, 0, 0);
-                }
-              }
+              for (int a = 0; a < NF; ++a) acc[a][b] = mfma_step<WT>(W[a][f], av, av, acc[a][b]);
             }
           }
         }
       }
     };
 
-    load_w(wA, 0);
-    load_a(0);
-    store_a(0);
+    uint4 wA[NF][FL], wB[NF][FL];
+    dma(0, 0);
+    ldw(wA, 0);
     for (int c = 0; c < nch; c += 2) {
-      const bool h1 = c + 1 < nch;
-      if (h1) {
-        load_w(wB, c + 1);
-        load_a(c + 1);
-      }
+      wait_vm0();
       __syncthreads();
+      if (c + 1 < nch) {
+        dma(c + 1, 1);
+        ldw(wB, c + 1);
+      }
       compute(wA, 0, c);
-      if (!h1) break;
-      store_a(1);
-      const bool h2 = c + 2 < nch;
-      if (h2) {
-        load_w(wA, c + 2);
-        load_a(c + 2);
-      }
+      if (c + 1 >= nch) break;
+      wait_vm0();
       __syncthreads();
+      if (c + 2 < nch) {
+        dma(c + 2, 0);
+        ldw(wA, c + 2);
+      }
       compute(wB, 1, c + 1);
-      if (h2) store_a(0);
     }
   }
 };
 
 // ---------------------------------------------------------------------------------
+// shared memory
+// ---------------------------------------------------------------------------------
+template <int WT, int MG> struct Smem {
+  union {
+    char act[2 * Core<WT, MG>::BUF];
+    struct {
+      int ids[256];
+      float wl[kWaves][kMaxK];
+      int hist[kMaxE];
+      int tmp[kMaxE];
+      int scan0[kMaxE + 1];
+      int scan1[kMaxE + 1];
+    } r;
+    f4 red[kWaves][64];
+  } u;
+  int rows[MG * 16];
+  int bcast[4];
+};
+
+// ---------------------------------------------------------------------------------
 // workgroup-level sync helpers
 // ---------------------------------------------------------------------------------
-// Every thread: make this workgroup's global writes visible at agent scope, then bump
-// `counter` once.  Returns the counter's old value (valid in thread 0 only).
+// Every thread: wait until this thread's device-coherent stores have completed, then (after
+// the barrier) bump `counter` once.  Returns the counter's old value (thread 0 only).
 __device__ __forceinline__ int wg_signal(int *counter) {
-  __threadfence();
+  wait_vm0();
   __syncthreads();
   int old = 0;
-  if (threadIdx.x == 0) old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (otid() == 0) old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return old;
 }
 
-template <int MG>
-__device__ __forceinline__ bool wg_wait(const int *p, int target, int *err, Smem<MG> &sm) {
+template <class SM>
+__device__ __forceinline__ bool wg_wait(const int *p, int target, int *err, SM &sm) {
   __syncthreads();
-  if (threadIdx.x == 0) sm.bcast[1] = spin_geq(p, target, err) ? 1 : 0;
+  if (otid() == 0) sm.bcast[1] = spin_geq(p, target, err) ? 1 : 0;
   __syncthreads();
-  const bool ok = sm.bcast[1] != 0;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return ok;
+  return uni(sm.bcast[1]) != 0;
 }
 
 // ---------------------------------------------------------------------------------
 // phase items
 // ---------------------------------------------------------------------------------
-template <int MG>
-__device__ void zero_item(const KParams &P, int i) {
+__device__ __forceinline__ void zero_item(const KParams &P, int i) {
   const int lo = i * kZeroPerItem;
-  for (int q = threadIdx.x; q < kZeroPerItem; q += kThreads) {
+  for (int q = otid(); q < kZeroPerItem; q += kThreads) {
     const int idx = lo + q;
-    if (idx < P.mt_cap) P.gudone[idx] = 0;
+    if (idx < P.mt_cap) st_coh(P.gudone + idx, 0);
   }
 }
 
-// router logits for 16 tokens x 64 experts
-template <int WT, int MG>
-__device__ void logits_item(const KParams &P, int i, Smem<MG> &sm) {
+// router logits for 16 tokens x 16 experts; wave w sums K range [w*d/4, (w+1)*d/4)
+template <int WT, class SM>
+__device__ __forceinline__ void logits_item(const KParams &P, int i, SM &sm) {
   constexpr int RT = (WT == WF32) ? WF32 : WBF16;  // the router runs in the activation dtype
-  using G = Gemm<RT, 1, 1>;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, j = lane & 15;
+  constexpr int KU = Ty<RT>::KU, ASZ = Ty<RT>::ASZ;
+  const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int lt = i / P.n_le, le = i % P.n_le;
   const int t0 = lt * kLogitTokens, e0 = le * kLogitExperts;
-  const int ntok = min(kLogitTokens, P.T - t0);
-  if (tid < 16) sm.rows[tid] = t0 + min(tid, ntok - 1);
-  __syncthreads();
-  const size_t asz = WTr<RT>::ASZ;
-  const int er = min(e0 + wave * 16 + j, P.E - 1);
-  const char *wrow[1] = {reinterpret_cast<const char *>(P.wr) + (size_t)er * P.d * asz + g * 16};
-  const float *sc[1] = {nullptr};
-  f4 acc[1][1];
-  G::run(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows,
-         reinterpret_cast<char(*)[16 * kRowChunkBytes]>(sm.u.g.act), P.d, 1);
-  if (j < ntok) {
-    const int t = t0 + j;
+  const int kq = P.d / kWaves, kbeg = wv * kq;
+  const int er = min(e0 + j, P.E - 1), tr = min(t0 + j, P.T - 1);
+  const char *wp = reinterpret_cast<const char *>(P.wr) + ((size_t)er * P.d + kbeg) * ASZ + g * 16;
+  const char *xp = reinterpret_cast<const char *>(P.x) + ((size_t)tr * P.d + kbeg) * ASZ + g * 16;
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  const int nsteps = kq / KU;
+  for (int s0 = 0; s0 < nsteps; s0 += 8) {
+    uint4 w[8], a[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = e0 + wave * 16 + 4 * g + r;
-      if (e < P.E) P.logits[(size_t)t * P.E + e] = acc[0][0][r] + (P.bias ? P.bias[e] : 0.f);
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, nsteps - 1);
+      w[u] = *reinterpret_cast<const uint4 *>(wp + (size_t)s * 64);
+      a[u] = *reinterpret_cast<const uint4 *>(xp + (size_t)s * 64);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < nsteps) acc = mfma_step<RT>(w[u], a[u], a[u], acc);
+  }
+  sm.u.red[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0) {
+    const f4 s = ((sm.u.red[0][lane] + sm.u.red[1][lane]) + sm.u.red[2][lane]) + sm.u.red[3][lane];
+    const int t = t0 + j;
+    if (t < P.T) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = e0 + 4 * g + r;
+        if (e < P.E) st_coh(P.logits + (size_t)t * P.E + e, s[r] + (P.bias ? P.bias[e] : 0.f));
+      }
     }
   }
 }
 
-// wave-level exclusive scan of in[0..N) -> out[0..N+1) (out[N] = total); one wave runs it
+// wave-level exclusive scan of in[0..N) -> out[0..N] (out[N] = total); one wave runs it
 __device__ void wave_excl_scan(const int *in, int *out, int N, int lane) {
   const int per = (N + 63) / 64;
   const int lo = min(lane * per, N), hi = min(lo + per, N);
@@ -407,10 +469,10 @@ __device__ void wave_excl_scan(const int *in, int *out, int N, int lane) {
 }
 
 // The plan: per-expert scan of the chunk histograms (chunk bases, in place), counts,
-// offsets, m-tile offsets.  One workgroup.
-template <int MG>
-__device__ void plan_wg(const KParams &P, Smem<MG> &sm) {
-  const int tid = threadIdx.x, E = P.E, nkc = P.n_kc;
+// offsets, m-tile offsets and the m-tile descriptor table.  One workgroup.
+template <class SM>
+__device__ void plan_wg(const KParams &P, SM &sm) {
+  const int tid = otid(), E = P.E, nkc = P.n_kc;
   int *cnt = sm.u.r.hist;
   int *mtc = sm.u.r.tmp;
   for (int e = tid; e < E; e += kThreads) {
@@ -418,10 +480,10 @@ __device__ void plan_wg(const KParams &P, Smem<MG> &sm) {
     for (int c0 = 0; c0 < nkc; c0 += 16) {
       int h[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) h[q] = (c0 + q < nkc) ? P.hist[(size_t)(c0 + q) * E + e] : 0;
+      for (int q = 0; q < 16; ++q) h[q] = (c0 + q < nkc) ? ld_coh(P.hist + (size_t)(c0 + q) * E + e) : 0;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        if (c0 + q < nkc) P.hist[(size_t)(c0 + q) * E + e] = run;
+        if (c0 + q < nkc) st_coh(P.hist + (size_t)(c0 + q) * E + e, run);
         run += h[q];
       }
     }
@@ -430,21 +492,32 @@ __device__ void plan_wg(const KParams &P, Smem<MG> &sm) {
   }
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63;
-  if (wave == 0) wave_excl_scan(cnt, P.offsets, E, lane);
-  if (wave == 1) wave_excl_scan(mtc, P.mtoff, E, lane);
-  for (int e = tid; e < E; e += kThreads) P.counts[e] = cnt[e];
+  // exclusive scans into LDS (counts -> offsets, m-tiles -> m-tile offsets), then publish
+  int *soff = sm.u.r.scan0;
+  int *smt = sm.u.r.scan1;
+  if (wave == 0) wave_excl_scan(cnt, soff, E, lane);
+  if (wave == 1) wave_excl_scan(mtc, smt, E, lane);
   __syncthreads();
-  if (tid == 0) P.ctrl[C_NMT] = P.mtoff[E];
-  wg_signal(P.ctrl + C_PLAN);
+  for (int e = tid; e <= E; e += kThreads) {
+    st_coh(P.offsets + e, soff[e]);
+    st_coh(P.mtoff + e, smt[e]);
+  }
+  for (int e = tid; e < E; e += kThreads) {
+    st_coh(P.counts + e, cnt[e]);
+    const int base = smt[e], off = soff[e], c = cnt[e];
+    for (int mt = 0; mt < mtc[e]; ++mt) st_coh_int4(P.desc + base + mt, make_int4(e, off + mt * P.bm, min(P.bm, c - mt * P.bm), 0));
+  }
+  if (tid == 0) st_coh(P.ctrl + kSlotInts * C_NMT, smt[E]);
+  wg_signal(P.ctrl + kSlotInts * C_PLAN);
 }
 
 // top-k + softmax + chunk histogram for tokens [c*tk, min(T, (c+1)*tk))
-template <int MG>
-__device__ void topk_item(const KParams &P, int c, Smem<MG> &sm) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+template <class SM>
+__device__ void topk_item(const KParams &P, int c, SM &sm) {
+  const int tid = otid(), wave = tid >> 6, lane = tid & 63;
   const int t0 = c * P.tk, ntok = min(P.tk, P.T - t0), k = P.k, E = P.E;
   if (P.phases & PH_IDS_GIVEN) {
-    for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = P.ids[(size_t)t0 * k + q];
+    for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = P.ids[(size_t)t0 * k + q];  // caller's input
   } else {
     for (int tt = wave; tt < ntok; tt += kWaves) {
       const int t = t0 + tt;
@@ -453,7 +526,7 @@ __device__ void topk_item(const KParams &P, int c, Smem<MG> &sm) {
 #pragma unroll
       for (int q = 0; q < kMaxE / 64; ++q) {
         const int e = q * 64 + lane;
-        key[q] = (e < E) ? ((uint64_t)ordered_key(Lr[e]) << 32) | (uint32_t)(E - 1 - e) : 0ull;
+        key[q] = (e < E) ? ((uint64_t)ordered_key(ld_coh(Lr + e)) << 32) | (uint32_t)(E - 1 - e) : 0ull;
       }
       for (int jj = 0; jj < k; ++jj) {
         uint64_t best = 0;
@@ -483,8 +556,8 @@ __device__ void topk_item(const KParams &P, int c, Smem<MG> &sm) {
           s += z;
         }
         for (int jj = 0; jj < k; ++jj) {
-          P.wts[(size_t)t * k + jj] = sm.u.r.wl[wave][jj] / s;
-          P.ids[(size_t)t * k + jj] = sm.u.r.ids[tt * k + jj];
+          st_coh(P.wts + (size_t)t * k + jj, sm.u.r.wl[wave][jj] / s);
+          st_coh(P.ids + (size_t)t * k + jj, sm.u.r.ids[tt * k + jj]);
         }
       }
     }
@@ -495,27 +568,24 @@ __device__ void topk_item(const KParams &P, int c, Smem<MG> &sm) {
   for (int q = tid; q < ntok * k; q += kThreads) {
     const int e = sm.u.r.ids[q];
     if (e >= 0 && e < E) atomicAdd(&sm.u.r.hist[e], 1);
-    else __hip_atomic_store(P.ctrl + C_ERR, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else __hip_atomic_store(P.ctrl + kSlotInts * C_ERR, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kThreads) P.hist[(size_t)c * E + e] = sm.u.r.hist[e];
-  const int old = wg_signal(P.ctrl + C_KDONE);
+  for (int e = tid; e < E; e += kThreads) st_coh(P.hist + (size_t)c * E + e, sm.u.r.hist[e]);
+  const int old = wg_signal(P.ctrl + kSlotInts * C_KDONE);
   if (tid == 0) sm.bcast[2] = (old == P.n_kc - 1) ? 1 : 0;
   __syncthreads();
-  if (sm.bcast[2] && (P.phases & PH_PERMUTE)) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    plan_wg(P, sm);
-  }
+  if (uni(sm.bcast[2]) && (P.phases & PH_PERMUTE)) plan_wg(P, sm);
 }
 
 // stable scatter of chunk c: position of slot (t, j) with expert e is
 //   offsets[e] + (slots of e in earlier chunks) + (slots of e in earlier tokens of this chunk)
-template <int MG>
-__device__ void scatter_item(const KParams &P, int c, Smem<MG> &sm) {
-  const int tid = threadIdx.x;
+template <class SM>
+__device__ void scatter_item(const KParams &P, int c, SM &sm) {
+  const int tid = otid();
   const int t0 = c * P.tk, ntok = min(P.tk, P.T - t0), k = P.k, E = P.E;
   const int nq = ntok * k;
-  for (int q = tid; q < nq; q += kThreads) sm.u.r.ids[q] = P.ids[(size_t)t0 * k + q];
+  for (int q = tid; q < nq; q += kThreads) sm.u.r.ids[q] = ld_coh(P.ids + (size_t)t0 * k + q);
   __syncthreads();
   for (int q = tid; q < nq; q += kThreads) {
     const int e = sm.u.r.ids[q];
@@ -523,44 +593,36 @@ __device__ void scatter_item(const KParams &P, int c, Smem<MG> &sm) {
     const int first = (q / k) * k;
     int rank = 0;
     for (int q2 = 0; q2 < first; ++q2) rank += (sm.u.r.ids[q2] == e) ? 1 : 0;
-    const int p = P.offsets[e] + P.hist[(size_t)c * E + e] + rank;
+    const int p = ld_coh(P.offsets + e) + ld_coh(P.hist + (size_t)c * E + e) + rank;
     const int slot = t0 * k + q;
-    P.perm[p] = slot;
-    P.inv_perm[slot] = p;
+    st_coh(P.perm + p, slot);
+    st_coh(P.inv_perm + slot, p);
   }
-}
-
-// which routed expert owns global m-tile g: the e with mtoff[e] <= g < mtoff[e+1]
-__device__ __forceinline__ int find_expert(const int *mtoff, int E, int g) {
-  int lo = 0, hi = E;  // upper_bound over mtoff[0..E]
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (mtoff[mid] <= g) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo - 1;
 }
 
 template <int WT> struct ActT { using type = uint16_t; };
 template <> struct ActT<WF32> { using type = float; };
 
+// 4 consecutive values of H or Y (device-coherent: read by other workgroups)
 template <int WT>
 __device__ __forceinline__ void store4(void *base, size_t idx, f4 v) {
   if constexpr (WT == WF32) {
-    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+    float *p = reinterpret_cast<float *>(base) + idx;
+    st_coh64(p, (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32));
+    st_coh64(p + 2, (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32));
   } else {
-    uint2 u;
-    u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(base) + idx) = u;
+    const uint64_t u = (uint64_t)f2bf(v[0]) | ((uint64_t)f2bf(v[1]) << 16) | ((uint64_t)f2bf(v[2]) << 32) |
+                       ((uint64_t)f2bf(v[3]) << 48);
+    st_coh64(reinterpret_cast<uint16_t *>(base) + idx, u);
   }
 }
 
-// gate/up item: rows (tokens) of one m-tile x 64 H columns; SwiGLU in registers
-template <int WT, int MG>
-__device__ void gateup_item(const KParams &P, bool shared, int i, Smem<MG> &sm) {
-  using G = Gemm<WT, 2, MG>;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, j = lane & 15;
+// gate/up item: rows (tokens) of one m-tile x gu_cols H columns; SwiGLU in registers
+template <int WT, int MG, class SM>
+__device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i, SM &sm) {
+  using C = Core<WT, MG>;
+  constexpr int NF = C::NF, NH = NF / 2;
+  const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int gm = i / P.nt_gu, nt = i % P.nt_gu;
   int e, row0, m, counter;
   size_t hrow0;
@@ -571,58 +633,67 @@ __device__ void gateup_item(const KParams &P, bool shared, int i, Smem<MG> &sm) 
     hrow0 = (size_t)P.T * P.k + row0;
     counter = gm;
   } else {
-    e = find_expert(P.mtoff, P.E, gm);
-    const int mt = gm - P.mtoff[e];
-    row0 = P.offsets[e] + mt * P.bm;
-    m = min(P.bm, P.counts[e] - mt * P.bm);
+    const int4 ds = ld_coh_int4(P.desc + gm);
+    e = uni(ds.x);
+    row0 = uni(ds.y);
+    m = uni(ds.z);
     hrow0 = row0;
     counter = P.n_shmt + gm;
   }
-  for (int r = tid; r < G::BMR; r += kThreads) {
+  for (int r = tid; r < C::BMR; r += kThreads) {
     const int rr = min(r, m - 1);
-    int tok = shared ? row0 + rr : P.perm[row0 + rr] / P.k;
-    tok = min(max(tok, 0), P.T - 1);
-    sm.rows[r] = tok;
+    int tok = shared ? row0 + rr : ld_coh(P.perm + row0 + rr) / P.k;
+    sm.rows[r] = min(max(tok, 0), P.T - 1);
   }
   __syncthreads();
-  const size_t wsz = WTr<WT>::WSZ, asz = WTr<WT>::ASZ;
-  const int n0 = nt * kGuCols + wave * 16;
+  const size_t wsz = Ty<WT>::WSZ, asz = Ty<WT>::ASZ;
+  const int n0 = nt * P.gu_cols + wv * NH * 16;
   const char *wgb = reinterpret_cast<const char *>(shared ? P.shg : P.wg);
   const char *wub = reinterpret_cast<const char *>(shared ? P.shu : P.wu);
   const size_t emat = shared ? 0 : (size_t)e * P.n * P.d * wsz;
-  const size_t rowoff = (size_t)(n0 + j) * P.d * wsz + g * 16;
-  const char *wrow[2] = {wgb + emat + rowoff, wub + emat + rowoff};
-  const float *sc[2] = {nullptr, nullptr};
-  if constexpr (WT == WFP8) {
-    const int nkb = P.d / 128;
-    const size_t soff = (shared ? 0 : (size_t)e * (P.n / 128) * nkb) + (size_t)(n0 / 128) * nkb;
-    sc[0] = (shared ? P.shsg : P.sg) + soff;
-    sc[1] = (shared ? P.shsu : P.su) + soff;
+  const char *wrow[NF];
+  const float *sc[NF];
+#pragma unroll
+  for (int a = 0; a < NH; ++a) {
+    const size_t rowoff = (size_t)(n0 + 16 * a + j) * P.d * wsz + g * 16;
+    wrow[a] = wgb + emat + rowoff;
+    wrow[a + NH] = wub + emat + rowoff;
+    sc[a] = sc[a + NH] = nullptr;
+    if constexpr (WT == WFP8) {
+      const int nkb = P.d / 128;
+      const size_t soff = (shared ? 0 : (size_t)e * (P.n / 128) * nkb) + (size_t)((n0 + 16 * a) / 128) * nkb;
+      sc[a] = (shared ? P.shsg : P.sg) + soff;
+      sc[a + NH] = (shared ? P.shsu : P.su) + soff;
+    }
   }
-  f4 acc[2][MG];
+  f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
-  G::run(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows,
-         reinterpret_cast<char(*)[G::BMR * kRowChunkBytes]>(sm.u.g.act), P.d, ngroups);
+  C::template run<false>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, sm.u.act, P.d,
+                         ngroups);
 #pragma unroll
   for (int b = 0; b < MG; ++b) {
     const int r = b * 16 + j;
     if (r < m) {
-      f4 h;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) h[q] = silu_mul(acc[0][b][q], acc[1][b][q]);
-      store4<WT>(P.H, (hrow0 + r) * (size_t)P.n + n0 + 4 * g, h);
+      for (int a = 0; a < NH; ++a) {
+        f4 h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h[q] = silu_mul(acc[a][b][q], acc[a + NH][b][q]);
+        store4<WT>(P.H, (hrow0 + r) * (size_t)P.n + n0 + 16 * a + 4 * g, h);
+      }
     }
   }
   wg_signal(P.gudone + counter);
 }
 
-// down item: rows of one m-tile x 128 output columns
-template <int WT, int MG>
-__device__ bool down_item(const KParams &P, int i, Smem<MG> &sm) {
-  using G = Gemm<WT, 2, MG>;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, j = lane & 15;
+// down item: rows of one m-tile x dn_cols output columns
+template <int WT, int MG, class SM>
+__device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm) {
+  using C = Core<WT, MG>;
+  constexpr int NF = C::NF;
+  const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int gm = i / P.nt_dn, dt = i % P.nt_dn;
-  if (!wg_wait(P.gudone + gm, P.nt_gu, P.ctrl + C_ERR, sm)) return false;
+  if (!wg_wait(P.gudone + gm, P.nt_gu, P.ctrl + kSlotInts * C_ERR, sm)) return false;
   const bool shared = gm < P.n_shmt;
   int e, m;
   size_t row0;
@@ -632,65 +703,67 @@ __device__ bool down_item(const KParams &P, int i, Smem<MG> &sm) {
     m = min(P.bm, P.T - t0);
     row0 = (size_t)P.T * P.k + t0;
   } else {
-    const int gr = gm - P.n_shmt;
-    e = find_expert(P.mtoff, P.E, gr);
-    const int mt = gr - P.mtoff[e];
-    row0 = (size_t)P.offsets[e] + mt * P.bm;
-    m = min(P.bm, P.counts[e] - mt * P.bm);
+    const int4 ds = ld_coh_int4(P.desc + gm - P.n_shmt);
+    e = uni(ds.x);
+    row0 = (size_t)uni(ds.y);
+    m = uni(ds.z);
   }
-  for (int r = tid; r < G::BMR; r += kThreads) sm.rows[r] = (int)(row0 + min(r, m - 1));
+  for (int r = tid; r < C::BMR; r += kThreads) sm.rows[r] = (int)(row0 + min(r, m - 1));
   __syncthreads();
-  const size_t wsz = WTr<WT>::WSZ, asz = WTr<WT>::ASZ;
-  const int d0 = dt * kDnCols + wave * 32;
+  const size_t wsz = Ty<WT>::WSZ, asz = Ty<WT>::ASZ;
+  const int d0 = dt * P.dn_cols + wv * NF * 16;
   const char *wdb = reinterpret_cast<const char *>(shared ? P.shd : P.wd);
   const size_t emat = shared ? 0 : (size_t)e * P.d * P.n * wsz;
-  const int r0 = min(d0 + j, P.d - 1), r1 = min(d0 + 16 + j, P.d - 1);
-  const char *wrow[2] = {wdb + emat + (size_t)r0 * P.n * wsz + g * 16,
-                         wdb + emat + (size_t)r1 * P.n * wsz + g * 16};
-  const float *sc[2] = {nullptr, nullptr};
-  if constexpr (WT == WFP8) {
-    const int nkb = P.n / 128;
-    const float *sb = (shared ? P.shsd : P.sd) + (shared ? 0 : (size_t)e * (P.d / 128) * nkb);
-    sc[0] = sb + (size_t)(min(d0, P.d - 1) / 128) * nkb;
-    sc[1] = sb + (size_t)(min(d0 + 16, P.d - 1) / 128) * nkb;
+  const char *wrow[NF];
+  const float *sc[NF];
+#pragma unroll
+  for (int a = 0; a < NF; ++a) {
+    const int rr = min(d0 + 16 * a + j, P.d - 1);
+    wrow[a] = wdb + emat + (size_t)rr * P.n * wsz + g * 16;
+    sc[a] = nullptr;
+    if constexpr (WT == WFP8) {
+      const int nkb = P.n / 128;
+      const float *sb = (shared ? P.shsd : P.sd) + (shared ? 0 : (size_t)e * (P.d / 128) * nkb);
+      sc[a] = sb + (size_t)(min(d0 + 16 * a, P.d - 1) / 128) * nkb;
+    }
   }
-  f4 acc[2][MG];
+  f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
-  G::run(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n * asz, sm.rows,
-         reinterpret_cast<char(*)[G::BMR * kRowChunkBytes]>(sm.u.g.act), P.n, ngroups);
+  C::template run<true>(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n * asz, sm.rows, sm.u.act, P.n,
+                        ngroups);
 #pragma unroll
   for (int b = 0; b < MG; ++b) {
     const int r = b * 16 + j;
     if (r < m) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
+      for (int a = 0; a < NF; ++a) {
         const int c = d0 + 16 * a + 4 * g;
         if (c < P.d) store4<WT>(P.Y, (row0 + r) * (size_t)P.d + c, acc[a][b]);
       }
     }
   }
-  wg_signal(P.ctrl + C_DDONE);
+  wg_signal(P.ctrl + kSlotInts * C_DDONE);
   return true;
 }
 
 // combine: out[t] = sum_j w[t,j] * Y[inv_perm[t*k+j]] (+ Y[T*k + t]), float32, slot order
-template <int WT, int MG>
-__device__ void combine_item(const KParams &P, int c, Smem<MG> &sm) {
+template <int WT>
+__device__ __forceinline__ void combine_item(const KParams &P, int c) {
   using A = typename ActT<WT>::type;
   constexpr int VEC = 16 / sizeof(A);
   const int t0 = c * kCombineTokens, ntok = min(kCombineTokens, P.T - t0);
   const int nv = P.d / VEC;
   const A *Y = reinterpret_cast<const A *>(P.Y);
   A *out = reinterpret_cast<A *>(P.out);
-  for (int q = threadIdx.x; q < ntok * nv; q += kThreads) {
+  for (int q = otid(); q < ntok * nv; q += kThreads) {
     const int t = t0 + q / nv, v = q % nv;
     float acc[VEC];
 #pragma unroll
     for (int z = 0; z < VEC; ++z) acc[z] = 0.f;
     for (int jj = 0; jj < P.k; ++jj) {
-      const float w = P.wts[(size_t)t * P.k + jj];
-      const int p = P.inv_perm[(size_t)t * P.k + jj];
-      const uint4 raw = *reinterpret_cast<const uint4 *>(Y + (size_t)p * P.d + v * VEC);
+      const float w = ld_coh(P.wts + (size_t)t * P.k + jj);
+      const int p = ld_coh(P.inv_perm + (size_t)t * P.k + jj);
+      const uint4 raw = ld_coh16(Y + (size_t)p * P.d + v * VEC);
       if constexpr (WT == WF32) {
         const float *f = reinterpret_cast<const float *>(&raw);
 #pragma unroll
@@ -702,7 +775,7 @@ __device__ void combine_item(const KParams &P, int c, Smem<MG> &sm) {
       }
     }
     if (P.S) {
-      const uint4 raw = *reinterpret_cast<const uint4 *>(Y + ((size_t)P.T * P.k + t) * P.d + v * VEC);
+      const uint4 raw = ld_coh16(Y + ((size_t)P.T * P.k + t) * P.d + v * VEC);
       if constexpr (WT == WF32) {
         const float *f = reinterpret_cast<const float *>(&raw);
 #pragma unroll
@@ -729,13 +802,21 @@ __device__ void combine_item(const KParams &P, int c, Smem<MG> &sm) {
 // ---------------------------------------------------------------------------------
 // the persistent kernel
 // ---------------------------------------------------------------------------------
+enum ItemKind : int { K_ZERO = 0, K_ROUTER = 1, K_TOPK = 2, K_SHGU = 3, K_SCATTER = 4, K_GU = 5, K_DN = 6, K_COMB = 7 };
+
+// register budget per kernel (waves per SIMD): 2 for the narrow tiles, 1 for the widest
+template <int WT, int MG> struct Occ {
+  static constexpr int waves = (MG == 8 || (MG == 4 && WT != WBF16)) ? 1 : 2;
+};
+
 template <int WT, int MG>
-__global__ __launch_bounds__(kThreads) void moe_persistent(KParams P) {
-  __shared__ Smem<MG> sm;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occ<WT, MG>::waves)))
+void moe_persistent(KParams P) {
+  __shared__ Smem<WT, MG> sm;
   const int tid = threadIdx.x;
   int *ctrl = P.ctrl;
-  int *err = ctrl + C_ERR;
-  if (ld_relaxed(ctrl + C_MAGIC) != kMagic) {
+  int *err = ctrl + kSlotInts * C_ERR;
+  if (ld_relaxed(ctrl + kSlotInts * C_MAGIC) != kMagic) {
     if (tid == 0) __hip_atomic_store(err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
@@ -746,102 +827,107 @@ __global__ __launch_bounds__(kThreads) void moe_persistent(KParams P) {
   const int n_S = (P.phases & PH_PERMUTE) ? P.n_kc : 0;
   const bool dyn = (P.phases & (PH_FFN | PH_COMBINE)) != 0;
   bool zero_seen = false, logits_seen = false, plan_seen = false, scat_seen = false, dn_seen = false;
-  int n_mt = 0;
+  int n_mt = -1;
   int step = 0;
+  int next = 0;
+  const bool dynamic = P.schedule == 0;
+  if (dynamic && tid == 0) next = __hip_atomic_fetch_add(ctrl + kSlotInts * C_TICKET, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (;;) {
     __syncthreads();
-    if (P.schedule == 0) {
-      if (tid == 0) sm.bcast[0] = __hip_atomic_fetch_add(ctrl + C_TICKET, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (dynamic) {
+      if (tid == 0) sm.bcast[0] = next;
       __syncthreads();
     }
-    int i = P.schedule == 0 ? sm.bcast[0] : (int)blockIdx.x + step * (int)gridDim.x;
+    const int ticket = dynamic ? uni(sm.bcast[0]) : (int)blockIdx.x + step * (int)gridDim.x;
     ++step;
+    // prefetch the next ticket; its value is read at the top of the next iteration
+    if (dynamic && tid == 0) next = __hip_atomic_fetch_add(ctrl + kSlotInts * C_TICKET, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t t_start = P.trace ? wall_clock64() : 0;
+    int kind = -1;
+    int i = ticket;
     if (i < n_Z) {
-      zero_item<MG>(P, i);
-      wg_signal(ctrl + C_ZDONE);
-      continue;
-    }
-    i -= n_Z;
-    if (i < n_L) {
-      logits_item<WT, MG>(P, i, sm);
-      wg_signal(ctrl + C_LDONE);
-      continue;
-    }
-    i -= n_L;
-    if (i < n_K) {
+      zero_item(P, i);
+      wg_signal(ctrl + kSlotInts * C_ZDONE);
+      kind = K_ZERO;
+    } else if ((i -= n_Z) < n_L) {
+      logits_item<WT>(P, i, sm);
+      wg_signal(ctrl + kSlotInts * C_LDONE);
+      kind = K_ROUTER;
+    } else if ((i -= n_L) < n_K) {
       if (!(P.phases & PH_IDS_GIVEN) && !logits_seen) {
-        if (!wg_wait(ctrl + C_LDONE, n_L, err, sm)) break;
+        if (!wg_wait(ctrl + kSlotInts * C_LDONE, n_L, err, sm)) break;
         logits_seen = true;
       }
-      topk_item<MG>(P, i, sm);
-      continue;
-    }
-    i -= n_K;
-    if (i < n_SG) {
+      topk_item(P, i, sm);
+      kind = K_TOPK;
+    } else if ((i -= n_K) < n_SG) {
       if (!zero_seen) {
-        if (!wg_wait(ctrl + C_ZDONE, n_Z, err, sm)) break;
+        if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
       }
       gateup_item<WT, MG>(P, true, i, sm);
-      continue;
-    }
-    i -= n_SG;
-    if (i < n_S) {
+      kind = K_SHGU;
+    } else if ((i -= n_SG) < n_S) {
       if (!plan_seen) {
-        if (!wg_wait(ctrl + C_PLAN, 1, err, sm)) break;
+        if (!wg_wait(ctrl + kSlotInts * C_PLAN, 1, err, sm)) break;
         plan_seen = true;
       }
-      scatter_item<MG>(P, i, sm);
-      wg_signal(ctrl + C_SDONE);
-      continue;
-    }
-    i -= n_S;
-    if (!dyn) break;
-    if (!plan_seen) {
-      if (!wg_wait(ctrl + C_PLAN, 1, err, sm)) break;
-      plan_seen = true;
-    }
-    if (n_mt == 0) n_mt = ld_relaxed(ctrl + C_NMT);
-    const int n_G = n_mt * P.nt_gu;
-    if (i < n_G) {
-      if (!scat_seen) {
-        if (!wg_wait(ctrl + C_SDONE, n_S, err, sm)) break;
-        scat_seen = true;
+      scatter_item(P, i, sm);
+      wg_signal(ctrl + kSlotInts * C_SDONE);
+      kind = K_SCATTER;
+    } else {
+      i -= n_S;
+      if (!dyn) break;
+      if (!plan_seen) {
+        if (!wg_wait(ctrl + kSlotInts * C_PLAN, 1, err, sm)) break;
+        plan_seen = true;
       }
-      if (!zero_seen) {
-        if (!wg_wait(ctrl + C_ZDONE, n_Z, err, sm)) break;
-        zero_seen = true;
+      if (n_mt < 0) n_mt = uni(ld_relaxed(ctrl + kSlotInts * C_NMT));
+      const int n_G = n_mt * P.nt_gu;
+      const int n_D = (n_mt + P.n_shmt) * P.nt_dn;
+      if (i < n_G) {
+        if (!scat_seen) {
+          if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S, err, sm)) break;
+          scat_seen = true;
+        }
+        if (!zero_seen) {
+          if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
+          zero_seen = true;
+        }
+        gateup_item<WT, MG>(P, false, i, sm);
+        kind = K_GU;
+      } else if ((i -= n_G) < n_D) {
+        if (!zero_seen) {  // the dependency counters must be cleared before they are read
+          if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
+          zero_seen = true;
+        }
+        if (!down_item<WT, MG>(P, i, sm)) break;
+        kind = K_DN;
+      } else if ((i -= n_D) < P.n_comb) {
+        if (!dn_seen) {
+          if (!wg_wait(ctrl + kSlotInts * C_DDONE, n_D, err, sm)) break;
+          dn_seen = true;
+        }
+        combine_item<WT>(P, i);
+        kind = K_COMB;
+      } else {
+        break;
       }
-      gateup_item<WT, MG>(P, false, i, sm);
-      continue;
     }
-    i -= n_G;
-    const int n_D = (n_mt + P.n_shmt) * P.nt_dn;
-    if (i < n_D) {
-      if (!zero_seen) {  // the dependency counters must be cleared before they are read
-        if (!wg_wait(ctrl + C_ZDONE, n_Z, err, sm)) break;
-        zero_seen = true;
-      }
-      if (!down_item<WT, MG>(P, i, sm)) break;
-      continue;
+    if (P.trace && tid == 0 && ticket < P.trace_cap) {
+      unsigned long long *rec = P.trace + 4 * (size_t)ticket;
+      rec[0] = t_start;
+      rec[1] = wall_clock64();
+      rec[2] = (unsigned long long)ticket;
+      rec[3] = ((unsigned long long)blockIdx.x << 32) | (unsigned)kind;
     }
-    i -= n_D;
-    if (i < P.n_comb) {
-      if (!dn_seen) {
-        if (!wg_wait(ctrl + C_DDONE, n_D, err, sm)) break;
-        dn_seen = true;
-      }
-      combine_item<WT, MG>(P, i, sm);
-      continue;
-    }
-    break;
   }
   // the last workgroup out resets the control block for the next call
   __syncthreads();
   if (tid == 0) {
-    const int old = add_acq_rel(ctrl + C_EXIT, 1);
+    const int old = __hip_atomic_fetch_add(ctrl + kSlotInts * C_EXIT, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (int)gridDim.x - 1) {
-      for (int s = C_TICKET; s <= C_NMT; ++s) ctrl[s] = 0;
+      for (int s = C_TICKET; s <= C_NMT; ++s) ctrl[kSlotInts * s] = 0;
       __threadfence();
     }
   }
@@ -849,7 +935,7 @@ __global__ __launch_bounds__(kThreads) void moe_persistent(KParams P) {
 
 __global__ void ws_init_kernel(int *ctrl, size_t nwords) {
   for (size_t q = blockIdx.x * (size_t)blockDim.x + threadIdx.x; q < nwords; q += (size_t)gridDim.x * blockDim.x)
-    ctrl[q] = (q == C_MAGIC) ? kMagic : 0;
+    ctrl[q] = (q == (size_t)kSlotInts * C_MAGIC) ? kMagic : 0;
 }
 
 // ---------------------------------------------------------------------------------
@@ -911,7 +997,6 @@ struct Call {
   const float *bias;
   const moe_weights *w;
   void *out;
-  const moe_route_out *ro;
   int32_t *ids_user;
   float *wts_user, *logits_user;
   const int32_t *ids_in;
@@ -930,8 +1015,11 @@ moe_status launch(const Call &c) {
   if (!c.ws || (reinterpret_cast<uintptr_t>(c.ws) & 255u)) return MOE_ERR_INVALID_ARGUMENT;
   const Layout L = make_layout(p);
   if (c.ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (c.opts && (c.opts->grid_wgs < 0 || c.opts->schedule < 0 || c.opts->schedule > 1))
-    return c.opts && c.opts->schedule == 2 ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARGUMENT;
+  if (c.opts) {
+    if (c.opts->schedule == 2) return MOE_ERR_UNSUPPORTED;
+    if (c.opts->grid_wgs < 0 || c.opts->schedule < 0 || c.opts->schedule > 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (c.opts->trace_bytes < 0 || (c.opts->trace && !aligned16(c.opts->trace))) return MOE_ERR_INVALID_ARGUMENT;
+  }
   if (p->T == 0) return MOE_OK;
 
   char *ws = static_cast<char *>(c.ws);
@@ -945,6 +1033,8 @@ moe_status launch(const Call &c) {
   P.phases = c.phases;
   P.bm = L.tiles.bm;
   P.tk = L.tiles.tk;
+  P.gu_cols = L.tiles.gu_cols;
+  P.dn_cols = L.tiles.dn_cols;
   P.n_lt = L.n_lt;
   P.n_le = L.n_le;
   P.n_kc = L.n_kc;
@@ -981,10 +1071,15 @@ moe_status launch(const Call &c) {
   P.inv_perm = c.invperm_user ? c.invperm_user : reinterpret_cast<int *>(ws + L.off_invperm);
   P.ctrl = reinterpret_cast<int *>(ws);
   P.gudone = reinterpret_cast<int *>(ws + L.off_gudone);
+  P.desc = reinterpret_cast<int4 *>(ws + L.off_desc);
   P.hist = reinterpret_cast<int *>(ws + L.off_hist);
   P.mtoff = reinterpret_cast<int *>(ws + L.off_mtoff);
   P.H = ws + L.off_h;
   P.Y = ws + L.off_y;
+  if (c.opts && c.opts->trace) {
+    P.trace = static_cast<unsigned long long *>(c.opts->trace);
+    P.trace_cap = c.opts->trace_bytes / 32;
+  }
 
   int n_items = 0;
   {
@@ -993,8 +1088,7 @@ moe_status launch(const Call &c) {
     const int n_K = (P.phases & (PH_ROUTE | PH_PERMUTE)) ? P.n_kc : 0;
     const int n_SG = (P.phases & PH_FFN) ? P.n_shmt * P.nt_gu : 0;
     const int n_S = (P.phases & PH_PERMUTE) ? P.n_kc : 0;
-    P.n_static = n_Z + n_L + n_K + n_SG + n_S;
-    n_items = P.n_static;
+    n_items = n_Z + n_L + n_K + n_SG + n_S;
     if (P.phases & PH_FFN)
       n_items += L.mt_routed_max * (P.nt_gu + P.nt_dn) + P.n_shmt * P.nt_dn + P.n_comb;
   }
@@ -1128,9 +1222,11 @@ moe_status moe_forward(const moe_problem *p, const void *hidden, const void *w_r
 moe_status moe_last_device_error(const void *ws, hipStream_t stream) {
   if (!ws) return MOE_ERR_INVALID_ARGUMENT;
   if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ERR_HIP;
-  int ctrl[C_NSLOTS];
-  if (hipMemcpy(ctrl, ws, sizeof(ctrl), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
-  if (ctrl[C_MAGIC] != kMagic || ctrl[C_ERR] != 0) return MOE_ERR_DEVICE_FAULT;
+  int magic = 0, err = 0;
+  const int *c = static_cast<const int *>(ws);
+  if (hipMemcpy(&magic, c + kSlotInts * C_MAGIC, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+  if (hipMemcpy(&err, c + kSlotInts * C_ERR, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+  if (magic != kMagic || err != 0) return MOE_ERR_DEVICE_FAULT;
   return MOE_OK;
 }
 

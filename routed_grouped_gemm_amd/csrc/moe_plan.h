@@ -15,20 +15,20 @@ namespace moe {
 
 constexpr int kThreads = 256;          // threads per workgroup (4 wave64)
 constexpr int kWaves = 4;
-constexpr int kCtrlBytes = 4096;       // control block at the start of the workspace
+constexpr int kSlotInts = 1024;        // control slots sit 4 KB apart (separate HBM channels)
+constexpr int kCtrlBytes = 16 * kSlotInts * 4;  // control block at the start of the workspace
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 256;
-constexpr int kLogitTokens = 16;       // router item: 16 tokens x 64 experts
-constexpr int kLogitExperts = 64;
-constexpr int kGuCols = 64;            // gate/up item: 64 H columns (16 per wave)
-constexpr int kDnCols = 128;           // down item: 128 output columns (32 per wave)
-constexpr int kCombineTokens = 4;      // combine item: 4 tokens
+constexpr int kLogitTokens = 16;       // router item: 16 tokens x 16 experts, K split over 4 waves
+constexpr int kLogitExperts = 16;
+constexpr int kCombineTokens = 1;      // combine item: 1 token
 constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroing item
 
-// control-block slots (int32 each)
+// control-block slots (one int32 each, at int index slot * kSlotInts): a poll of one
+// counter never shares a cache line or channel with the ticket counter or another counter
 enum CtrlSlot : int {
   C_MAGIC = 0, C_TICKET = 1, C_ZDONE = 2, C_LDONE = 3, C_KDONE = 4, C_PLAN = 5, C_SDONE = 6,
-  C_DDONE = 7, C_EXIT = 8, C_NMT = 9, C_ERR = 16, C_NSLOTS = 32
+  C_DDONE = 7, C_EXIT = 8, C_NMT = 9, C_ERR = 10, C_NSLOTS = 16
 };
 constexpr int kMagic = 0x4d6f4531;     // "MoE1"
 
@@ -38,6 +38,9 @@ enum PhaseBits : int { PH_ROUTE = 1, PH_PERMUTE = 2, PH_FFN = 4, PH_COMBINE = 8,
 struct Tiles {
   int mg;          // 16-row token groups per m-tile (1, 2, 4 or 8)
   int bm;          // rows per m-tile = 16 * mg
+  int nf;          // 16-row weight fragments per wave (2 when mg == 1, else 4)
+  int gu_cols;     // H columns per gate/up item: 4 waves x nf/2 x 16
+  int dn_cols;     // output columns per down item: 4 waves x nf x 16
   int tk;          // tokens per top-k / scatter chunk (tk * k <= 256)
 };
 
@@ -53,7 +56,7 @@ struct Layout {
   int n_zero;            // counter-clearing items
   int64_t rows_h;        // rows of H and Y: T*k + n_shared*T
   // byte offsets into the workspace
-  size_t off_gudone, off_logits, off_ids, off_wts, off_hist, off_counts, off_offsets, off_mtoff,
+  size_t off_gudone, off_desc, off_logits, off_ids, off_wts, off_hist, off_counts, off_offsets, off_mtoff,
       off_perm, off_invperm, off_h, off_y, total;
 };
 
@@ -89,6 +92,9 @@ inline Tiles choose_tiles(const moe_problem *p) {
   const double mean_rows = p->E > 0 ? double(p->T) * p->k / p->E : 0.0;
   t.mg = mean_rows <= 16 ? 1 : mean_rows <= 32 ? 2 : mean_rows <= 64 ? 4 : 8;
   t.bm = 16 * t.mg;
+  t.nf = t.mg == 1 ? 2 : 4;
+  t.gu_cols = 4 * (t.nf / 2) * 16;
+  t.dn_cols = 4 * t.nf * 16;
   t.tk = 256 / p->k;
   if (t.tk < 1) t.tk = 1;
   return t;
@@ -109,8 +115,8 @@ inline Layout make_layout(const moe_problem *p) {
   if (bound > tk) bound = tk;
   L.mt_routed_max = (int)bound;
   L.n_shmt = p->n_shared ? (int)ceil_div(T, bm) : 0;
-  L.nt_gu = p->n / kGuCols;
-  L.nt_dn = (int)ceil_div(p->d, kDnCols);
+  L.nt_gu = p->n / L.tiles.gu_cols;
+  L.nt_dn = (int)ceil_div(p->d, L.tiles.dn_cols);
   L.n_comb = (int)ceil_div(T, kCombineTokens);
   L.n_zero = (int)ceil_div(L.mt_routed_max + L.n_shmt, kZeroPerItem);
   L.rows_h = tk + (int64_t)p->n_shared * T;
@@ -122,6 +128,7 @@ inline Layout make_layout(const moe_problem *p) {
     return at;
   };
   L.off_gudone = take(sizeof(int32_t) * (size_t)(L.mt_routed_max + L.n_shmt + 1));
+  L.off_desc = take(4 * sizeof(int32_t) * (size_t)(L.mt_routed_max + 1));
   L.off_logits = take(sizeof(float) * (size_t)(T * E));
   L.off_ids = take(sizeof(int32_t) * (size_t)tk);
   L.off_wts = take(sizeof(float) * (size_t)tk);

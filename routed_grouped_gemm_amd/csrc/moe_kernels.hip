@@ -59,14 +59,19 @@ template <> struct Ty<WFP8> { static constexpr int KU = 64, WSZ = 1, ASZ = 2; };
 // FL 16-byte weight loads per fragment per K chunk
 template <int WT, int MG> struct Shape {
   static constexpr int NF = MG == 1 ? 2 : 4;
-  static constexpr int FL = WT == WFP8 ? (MG == 1 ? 4 : 2) : (MG == 1 ? 8 : 4);
+  // register/LDS buffers: three (two K chunks in flight) where the registers allow it,
+  // else two (one chunk in flight, longer chunks)
+  static constexpr int NBUF = (MG == 1 || (MG == 2 && WT != WFP8)) ? 3 : 2;
+  static constexpr int FL = WT == WFP8 ? 2 : (MG == 1 || NBUF == 2) ? 4 : 2;
 };
 
 struct KParams {
   int T, d, n, E, k, S;
   int phases;
   int bm, tk, gu_cols, dn_cols;
-  int n_lt, n_le, n_kc, n_shmt, nt_gu, nt_dn, n_comb, n_zero, mt_cap;
+  int n_lt, n_le, n_kt, n_kc, n_shmt, nt_gu, nt_dn, n_comb, mt_cap;
+  int n_Z, n_L, n_K, n_SG, n_S;   // items per static phase (ticket order Z, L, K, SG, S)
+  int gd_words, hist_words;       // words cleared by the Z items
   int schedule;  // 0 dynamic, 1 static
   const void *x, *wr;
   const float *bias;
@@ -100,8 +105,14 @@ __device__ __forceinline__ int otid() {
   return t;
 }
 
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima): at most N vector memory
+// operations of this wave still outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_vm0() { wait_vm<0>(); }
 
 // 16 bytes per lane, global -> LDS; lane l lands at lds_base + 16*l (lds_base uniform).
 // COH selects the device-coherent cache policy (SC1) for data written in this launch.
@@ -155,7 +166,7 @@ constexpr uint64_t kSpinTicks = 200000000ull;  // ~2 s of the 100 MHz wall clock
 // poll); the caller issues one acquire fence after the wait succeeds.  Polls back off
 // from ~0.1 us to ~0.9 us apart: hundreds of waiting workgroups polling one address at full
 // rate would saturate that address's memory channel and slow every other load.
-__device__ bool spin_geq(const int *p, int target, int *err) {
+__device__ __forceinline__ bool spin_geq(const int *p, int target, int *err) {
   if (ld_relaxed(p) >= target) return true;
   const uint64_t t0 = wall_clock64();
   for (int it = 0;; ++it) {
@@ -239,7 +250,69 @@ template <int WT, int MG> struct Core {
   static constexpr int RPK = 1024 / RB;         // rows per 1 KB load-to-LDS block
   static constexpr int NDMA = BMR * RB / 1024 / kWaves;
   static constexpr int BUF = BMR * RB;          // bytes of one LDS buffer
+  static constexpr int NBUF = Shape<WT, MG>::NBUF;
+  static constexpr int PER_CHUNK = NDMA + NF * FL;  // vector memory ops per wave per chunk
   static_assert(NDMA >= 1 && RPK >= 1, "tile shape");
+
+  // the MFMAs of one K chunk; FULL: every token group is present (no per-group branch,
+  // so LDS reads and MFMAs of different groups interleave freely)
+  template <bool FULL>
+  __device__ static __forceinline__ void chunk_mfma(f4 (&acc)[NF][MG], const uint4 (&W)[NF][FL], const char *A,
+                                                    const float *const (&sc)[NF], int c, int ngroups, int g, int j) {
+    if constexpr (WT == WFP8) {
+      constexpr int BPC = FL / 2;             // 128-wide scale blocks per chunk
+      constexpr int MGC = MG < 4 ? MG : 4;    // token groups per partial-sum pass
+#pragma unroll
+      for (int blk = 0; blk < BPC; ++blk) {
+        float s[NF];
+#pragma unroll
+        for (int a = 0; a < NF; ++a) s[a] = sc[a][c * BPC + blk];
+#pragma unroll
+        for (int b0 = 0; b0 < MG; b0 += MGC) {
+          if (FULL || b0 < ngroups) {
+            f4 tmp[NF][MGC];
+#pragma unroll
+            for (int a = 0; a < NF; ++a)
+#pragma unroll
+              for (int b = 0; b < MGC; ++b) tmp[a][b] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ff = 0; ff < 2; ++ff) {
+              const int f = blk * 2 + ff;
+#pragma unroll
+              for (int b = 0; b < MGC; ++b) {
+                if (FULL || b0 + b < ngroups) {
+                  const int r = (b0 + b) * 16 + j;
+                  const int c0 = f * 8 + 2 * g;
+                  const uint4 a0 = *reinterpret_cast<const uint4 *>(A + r * RB + ((c0 ^ (r & (NCOL - 1))) << 4));
+                  const uint4 a1 = *reinterpret_cast<const uint4 *>(A + r * RB + (((c0 + 1) ^ (r & (NCOL - 1))) << 4));
+#pragma unroll
+                  for (int a = 0; a < NF; ++a) tmp[a][b] = mfma_step<WT>(W[a][f], a0, a1, tmp[a][b]);
+                }
+              }
+            }
+#pragma unroll
+            for (int a = 0; a < NF; ++a)
+#pragma unroll
+              for (int b = 0; b < MGC; ++b) acc[a][b0 + b] += tmp[a][b] * s[a];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int f = 0; f < FL; ++f) {
+#pragma unroll
+        for (int b = 0; b < MG; ++b) {
+          if (FULL || b < ngroups) {
+            const int r = b * 16 + j;
+            const int c0 = f * 4 + g;
+            const uint4 av = *reinterpret_cast<const uint4 *>(A + r * RB + ((c0 ^ (r & (NCOL - 1))) << 4));
+#pragma unroll
+            for (int a = 0; a < NF; ++a) acc[a][b] = mfma_step<WT>(W[a][f], av, av, acc[a][b]);
+          }
+        }
+      }
+    }
+  }
 
   // COH: the activation rows were written earlier in this launch (H), so they are read
   // with the device-coherent policy
@@ -276,81 +349,71 @@ template <int WT, int MG> struct Core {
     };
     auto compute = [&](const uint4(&W)[NF][FL], int buf, int c) {
       const char *A = lds + buf * BUF;
-      if constexpr (WT == WFP8) {
-        constexpr int BPC = FL / 2;             // 128-wide scale blocks per chunk
-        constexpr int MGC = MG < 4 ? MG : 4;    // token groups per partial-sum pass
-#pragma unroll
-        for (int blk = 0; blk < BPC; ++blk) {
-          float s[NF];
-#pragma unroll
-          for (int a = 0; a < NF; ++a) s[a] = sc[a][c * BPC + blk];
-#pragma unroll
-          for (int b0 = 0; b0 < MG; b0 += MGC) {
-            if (b0 < ngroups) {
-              f4 tmp[NF][MGC];
-#pragma unroll
-              for (int a = 0; a < NF; ++a)
-#pragma unroll
-                for (int b = 0; b < MGC; ++b) tmp[a][b] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int ff = 0; ff < 2; ++ff) {
-                const int f = blk * 2 + ff;
-#pragma unroll
-                for (int b = 0; b < MGC; ++b) {
-                  if (b0 + b < ngroups) {
-                    const int r = (b0 + b) * 16 + j;
-                    const int c0 = f * 8 + 2 * g;
-                    const uint4 a0 = *reinterpret_cast<const uint4 *>(A + r * RB + ((c0 ^ (r & (NCOL - 1))) << 4));
-                    const uint4 a1 =
-                        *reinterpret_cast<const uint4 *>(A + r * RB + (((c0 + 1) ^ (r & (NCOL - 1))) << 4));
-#pragma unroll
-                    for (int a = 0; a < NF; ++a) tmp[a][b] = mfma_step<WT>(W[a][f], a0, a1, tmp[a][b]);
-                  }
-                }
-              }
-#pragma unroll
-              for (int a = 0; a < NF; ++a)
-#pragma unroll
-                for (int b = 0; b < MGC; ++b) acc[a][b0 + b] += tmp[a][b] * s[a];
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int f = 0; f < FL; ++f) {
-#pragma unroll
-          for (int b = 0; b < MG; ++b) {
-            if (b < ngroups) {
-              const int r = b * 16 + j;
-              const int c0 = f * 4 + g;
-              const uint4 av = *reinterpret_cast<const uint4 *>(A + r * RB + ((c0 ^ (r & (NCOL - 1))) << 4));
-#pragma unroll
-              for (int a = 0; a < NF; ++a) acc[a][b] = mfma_step<WT>(W[a][f], av, av, acc[a][b]);
-            }
-          }
-        }
-      }
+      // small tiles compute every token group (rows past the tile's end repeat its last
+      // row, valid data whose results are not stored); large tiles skip absent groups,
+      // which also keeps the compiler from hoisting every LDS read of the chunk at once
+      chunk_mfma<(MG <= 2)>(acc, W, A, sc, c, ngroups, g, j);
     };
 
-    uint4 wA[NF][FL], wB[NF][FL];
-    dma(0, 0);
-    ldw(wA, 0);
-    for (int c = 0; c < nch; c += 2) {
-      wait_vm0();
-      __syncthreads();
-      if (c + 1 < nch) {
-        dma(c + 1, 1);
-        ldw(wB, c + 1);
+    if constexpr (NBUF == 2) {
+      // one chunk in flight: wait for everything, then issue the next chunk and compute
+      uint4 wA[NF][FL], wB[NF][FL];
+      dma(0, 0);
+      ldw(wA, 0);
+      for (int c = 0; c < nch; c += 2) {
+        wait_vm0();
+        __syncthreads();
+        if (c + 1 < nch) {
+          dma(c + 1, 1);
+          ldw(wB, c + 1);
+        }
+        compute(wA, 0, c);
+        if (c + 1 >= nch) break;
+        wait_vm0();
+        __syncthreads();
+        if (c + 2 < nch) {
+          dma(c + 2, 0);
+          ldw(wA, c + 2);
+        }
+        compute(wB, 1, c + 1);
       }
-      compute(wA, 0, c);
-      if (c + 1 >= nch) break;
-      wait_vm0();
-      __syncthreads();
-      if (c + 2 < nch) {
-        dma(c + 2, 0);
-        ldw(wA, c + 2);
+    } else {
+      // two chunks in flight: wait only for the oldest one (vmcnt counts this wave's
+      // outstanding operations in issue order), then refill the buffer freed by the
+      // previous step; the barrier also tells every wave that the LDS buffer about to be
+      // refilled has been read by all of them
+      uint4 w0[NF][FL], w1[NF][FL], w2[NF][FL];
+      dma(0, 0);
+      ldw(w0, 0);
+      if (nch > 1) {
+        dma(1, 1);
+        ldw(w1, 1);
       }
-      compute(wB, 1, c + 1);
+      for (int c = 0; c < nch; c += 3) {
+        if (c + 1 < nch) wait_vm<PER_CHUNK>(); else wait_vm0();
+        __syncthreads();
+        if (c + 2 < nch) {
+          dma(c + 2, 2);
+          ldw(w2, c + 2);
+        }
+        compute(w0, 0, c);
+        if (c + 1 >= nch) break;
+        if (c + 2 < nch) wait_vm<PER_CHUNK>(); else wait_vm0();
+        __syncthreads();
+        if (c + 3 < nch) {
+          dma(c + 3, 0);
+          ldw(w0, c + 3);
+        }
+        compute(w1, 1, c + 1);
+        if (c + 2 >= nch) break;
+        if (c + 3 < nch) wait_vm<PER_CHUNK>(); else wait_vm0();
+        __syncthreads();
+        if (c + 4 < nch) {
+          dma(c + 4, 1);
+          ldw(w1, c + 4);
+        }
+        compute(w2, 2, c + 2);
+      }
     }
   }
 };
@@ -359,20 +422,25 @@ template <int WT, int MG> struct Core {
 // shared memory
 // ---------------------------------------------------------------------------------
 template <int WT, int MG> struct Smem {
+  static_assert(MG == 1 || Core<(WT == WF32 ? WF32 : WBF16), (MG > 4 ? 4 : MG)>::NBUF *
+                                   Core<(WT == WF32 ? WF32 : WBF16), (MG > 4 ? 4 : MG)>::BUF <=
+                               Core<WT, MG>::NBUF * Core<WT, MG>::BUF,
+                "router tile must fit the activation buffers");
   union {
-    char act[2 * Core<WT, MG>::BUF];
+    char act[Core<WT, MG>::NBUF * Core<WT, MG>::BUF];
     struct {
-      int ids[256];
-      float wl[kWaves][kMaxK];
-      int hist[kMaxE];
-      int tmp[kMaxE];
-      int scan0[kMaxE + 1];
-      int scan1[kMaxE + 1];
+      int ids[kTopkTokens * kMaxK > kMaxChunkSlots ? kTopkTokens * kMaxK : kMaxChunkSlots];  // ids, slot order
+      int hist[kMaxE];                         // per-expert slot counts of the chunk
+      int tmp[kMaxE];                          // per-expert m-tile counts (plan)
+      int scan0[kMaxE + 1];                    // offsets (plan)
+      int scan1[kMaxE + 1];                    // m-tile offsets (plan)
+      uint32_t mask[kMaxE][kMaxChunkTokens / 32];  // tokens of the chunk that chose expert e
     } r;
     f4 red[kWaves][64];
   } u;
   int rows[MG * 16];
   int bcast[4];
+  uint32_t mark[2];  // trace: clock at the start and end of the tile loop of this item
 };
 
 // ---------------------------------------------------------------------------------
@@ -403,53 +471,95 @@ __device__ __forceinline__ void zero_item(const KParams &P, int i) {
   const int lo = i * kZeroPerItem;
   for (int q = otid(); q < kZeroPerItem; q += kThreads) {
     const int idx = lo + q;
-    if (idx < P.mt_cap) st_coh(P.gudone + idx, 0);
+    if (idx < P.gd_words) st_coh(P.gudone + idx, 0);
+    else if (idx - P.gd_words < P.hist_words) st_coh(P.hist + (idx - P.gd_words), 0);
   }
 }
 
-// router logits for 16 tokens x 16 experts; wave w sums K range [w*d/4, (w+1)*d/4)
+// router logits, decode-sized tiles: 16 tokens x 16 experts; wave w sums the K range
+// [w*d/4, (w+1)*d/4), then the four partial sums are added in wave order
 template <int WT, class SM>
-__device__ __forceinline__ void logits_item(const KParams &P, int i, SM &sm) {
+__device__ __forceinline__ void logits_item_split(const KParams &P, int i, SM &sm) {
   constexpr int RT = (WT == WF32) ? WF32 : WBF16;  // the router runs in the activation dtype
   constexpr int KU = Ty<RT>::KU, ASZ = Ty<RT>::ASZ;
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int lt = i / P.n_le, le = i % P.n_le;
-  const int t0 = lt * kLogitTokens, e0 = le * kLogitExperts;
+  const int t0 = lt * 16, e0 = le * 16;
   const int kq = P.d / kWaves, kbeg = wv * kq;
   const int er = min(e0 + j, P.E - 1), tr = min(t0 + j, P.T - 1);
   const char *wp = reinterpret_cast<const char *>(P.wr) + ((size_t)er * P.d + kbeg) * ASZ + g * 16;
   const char *xp = reinterpret_cast<const char *>(P.x) + ((size_t)tr * P.d + kbeg) * ASZ + g * 16;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
   const int nsteps = kq / KU;
-  for (int s0 = 0; s0 < nsteps; s0 += 8) {
-    uint4 w[8], a[8];
+  for (int s0 = 0; s0 < nsteps; s0 += 16) {
+    uint4 w[16], a[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = min(s0 + u, nsteps - 1);
-      w[u] = *reinterpret_cast<const uint4 *>(wp + (size_t)s * 64);
-      a[u] = *reinterpret_cast<const uint4 *>(xp + (size_t)s * 64);
+    for (int u = 0; u < 16; ++u) {
+      const int st = min(s0 + u, nsteps - 1);
+      w[u] = *reinterpret_cast<const uint4 *>(wp + (size_t)st * 64);
+      a[u] = *reinterpret_cast<const uint4 *>(xp + (size_t)st * 64);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 16; ++u)
       if (s0 + u < nsteps) acc = mfma_step<RT>(w[u], a[u], a[u], acc);
   }
   sm.u.red[wv][lane] = acc;
   __syncthreads();
   if (wv == 0) {
-    const f4 s = ((sm.u.red[0][lane] + sm.u.red[1][lane]) + sm.u.red[2][lane]) + sm.u.red[3][lane];
+    const f4 sum = ((sm.u.red[0][lane] + sm.u.red[1][lane]) + sm.u.red[2][lane]) + sm.u.red[3][lane];
     const int t = t0 + j;
     if (t < P.T) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int e = e0 + 4 * g + r;
-        if (e < P.E) st_coh(P.logits + (size_t)t * P.E + e, s[r] + (P.bias ? P.bias[e] : 0.f));
+        if (e < P.E) st_coh(P.logits + (size_t)t * P.E + e, sum[r] + (P.bias ? P.bias[e] : 0.f));
       }
     }
   }
 }
 
+// router logits, wide tiles: bm tokens x 64*NF experts on the expert tile core (router
+// rows are the weight operand, token rows the activation operand)
+template <int WT, int MG, class SM>
+__device__ __forceinline__ void logits_item_tile(const KParams &P, int i, SM &sm) {
+  constexpr int RT = (WT == WF32) ? WF32 : WBF16;
+  constexpr int RMG = MG > 4 ? 4 : MG;  // at most 64 tokens per router tile (register budget)
+  using C = Core<RT, RMG>;
+  constexpr int NF = C::NF;
+  const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
+  const int lt = i / P.n_le, le = i % P.n_le;
+  const int t0 = lt * C::BMR, e0 = le * (64 * NF) + wv * 16 * NF;
+  const int m = min(C::BMR, P.T - t0);
+  for (int r = tid; r < C::BMR; r += kThreads) sm.rows[r] = t0 + min(r, m - 1);
+  __syncthreads();
+  const size_t asz = Ty<RT>::ASZ;
+  const char *wrow[NF];
+  const float *sc[NF];
+#pragma unroll
+  for (int a = 0; a < NF; ++a) {
+    const int er = min(e0 + 16 * a + j, P.E - 1);
+    wrow[a] = reinterpret_cast<const char *>(P.wr) + (size_t)er * P.d * asz + g * 16;
+    sc[a] = nullptr;
+  }
+  f4 acc[NF][RMG];
+  C::template run<false>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, sm.u.act, P.d,
+                         (m + 15) >> 4);
+#pragma unroll
+  for (int a = 0; a < NF; ++a) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = e0 + 16 * a + 4 * g + r;
+      if (e >= P.E) continue;
+      const float bv = P.bias ? P.bias[e] : 0.f;
+#pragma unroll
+      for (int b = 0; b < RMG; ++b)
+        if (b * 16 + j < m) st_coh(P.logits + (size_t)(t0 + b * 16 + j) * P.E + e, acc[a][b][r] + bv);
+    }
+  }
+}
+
 // wave-level exclusive scan of in[0..N) -> out[0..N] (out[N] = total); one wave runs it
-__device__ void wave_excl_scan(const int *in, int *out, int N, int lane) {
+__device__ __forceinline__ void wave_excl_scan(const int *in, int *out, int N, int lane) {
   const int per = (N + 63) / 64;
   const int lo = min(lane * per, N), hi = min(lo + per, N);
   int s = 0;
@@ -468,23 +578,55 @@ __device__ void wave_excl_scan(const int *in, int *out, int N, int lane) {
   if (lane == 63) out[N] = incl;
 }
 
-// The plan: per-expert scan of the chunk histograms (chunk bases, in place), counts,
-// offsets, m-tile offsets and the m-tile descriptor table.  One workgroup.
+// max of a 64-bit key over the wave, in every lane: the row-shift / row-broadcast DPP
+// reduction (VALU data movement, no LDS round trips), result read from lane 63
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+#define MOE_DPP_MAX(CTRL, ROWM, BANKM)                                                      \
+  {                                                                                        \
+    const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWM, BANKM, false);    \
+    const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWM, BANKM, false);    \
+    const uint64_t o = ((uint64_t)ohi << 32) | olo, c = ((uint64_t)hi << 32) | lo;         \
+    if (o > c) {                                                                           \
+      lo = olo;                                                                            \
+      hi = ohi;                                                                            \
+    }                                                                                      \
+  }
+  MOE_DPP_MAX(0x111, 0xf, 0xf)  // row_shr:1
+  MOE_DPP_MAX(0x112, 0xf, 0xf)  // row_shr:2
+  MOE_DPP_MAX(0x113, 0xf, 0xf)  // row_shr:3
+  MOE_DPP_MAX(0x114, 0xf, 0xe)  // row_shr:4
+  MOE_DPP_MAX(0x118, 0xf, 0xc)  // row_shr:8
+  MOE_DPP_MAX(0x142, 0xa, 0xf)  // row_bcast:15
+  MOE_DPP_MAX(0x143, 0xc, 0xf)  // row_bcast:31
+#undef MOE_DPP_MAX
+  const uint32_t rlo = __builtin_amdgcn_readlane(lo, 63), rhi = __builtin_amdgcn_readlane(hi, 63);
+  return ((uint64_t)rhi << 32) | rlo;
+}
+
+// The plan: counts -> offsets (exclusive scan), m-tile counts -> m-tile offsets, the
+// m-tile descriptor table, and (several chunks) each chunk's per-expert base: the slots
+// of that expert in earlier chunks, written over the chunk histograms.  One workgroup.
+// from_lds: the single chunk's histogram is in sm.u.r.hist (no global round trip).
 template <class SM>
-__device__ void plan_wg(const KParams &P, SM &sm) {
+__device__ __forceinline__ void plan_wg(const KParams &P, SM &sm, bool from_lds) {
   const int tid = otid(), E = P.E, nkc = P.n_kc;
   int *cnt = sm.u.r.hist;
   int *mtc = sm.u.r.tmp;
   for (int e = tid; e < E; e += kThreads) {
     int run = 0;
-    for (int c0 = 0; c0 < nkc; c0 += 16) {
-      int h[16];
+    if (from_lds) {
+      run = cnt[e];
+    } else {
+      for (int c0 = 0; c0 < nkc; c0 += 32) {
+        int h[32];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) h[q] = (c0 + q < nkc) ? ld_coh(P.hist + (size_t)(c0 + q) * E + e) : 0;
+        for (int q = 0; q < 32; ++q) h[q] = (c0 + q < nkc) ? ld_coh(P.hist + (size_t)(c0 + q) * E + e) : 0;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        if (c0 + q < nkc) st_coh(P.hist + (size_t)(c0 + q) * E + e, run);
-        run += h[q];
+        for (int q = 0; q < 32; ++q) {
+          if (c0 + q < nkc) st_coh(P.hist + (size_t)(c0 + q) * E + e, run);
+          run += h[q];
+        }
       }
     }
     cnt[e] = run;
@@ -492,7 +634,6 @@ __device__ void plan_wg(const KParams &P, SM &sm) {
   }
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63;
-  // exclusive scans into LDS (counts -> offsets, m-tiles -> m-tile offsets), then publish
   int *soff = sm.u.r.scan0;
   int *smt = sm.u.r.scan1;
   if (wave == 0) wave_excl_scan(cnt, soff, E, lane);
@@ -508,96 +649,202 @@ __device__ void plan_wg(const KParams &P, SM &sm) {
     for (int mt = 0; mt < mtc[e]; ++mt) st_coh_int4(P.desc + base + mt, make_int4(e, off + mt * P.bm, min(P.bm, c - mt * P.bm), 0));
   }
   if (tid == 0) st_coh(P.ctrl + kSlotInts * C_NMT, smt[E]);
-  wg_signal(P.ctrl + kSlotInts * C_PLAN);
 }
 
-// top-k + softmax + chunk histogram for tokens [c*tk, min(T, (c+1)*tk))
+// chunk histogram and per-expert token bitmasks from the chunk's ids in sm.u.r.ids
 template <class SM>
-__device__ void topk_item(const KParams &P, int c, SM &sm) {
-  const int tid = otid(), wave = tid >> 6, lane = tid & 63;
-  const int t0 = c * P.tk, ntok = min(P.tk, P.T - t0), k = P.k, E = P.E;
-  if (P.phases & PH_IDS_GIVEN) {
-    for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = P.ids[(size_t)t0 * k + q];  // caller's input
-  } else {
-    for (int tt = wave; tt < ntok; tt += kWaves) {
-      const int t = t0 + tt;
-      const float *Lr = P.logits + (size_t)t * E;
-      uint64_t key[kMaxE / 64];
+__device__ __forceinline__ void chunk_masks(const KParams &P, int ntok, SM &sm) {
+  const int tid = otid(), k = P.k, E = P.E;
+  for (int e = tid; e < E; e += kThreads) {
+    sm.u.r.hist[e] = 0;
 #pragma unroll
-      for (int q = 0; q < kMaxE / 64; ++q) {
-        const int e = q * 64 + lane;
-        key[q] = (e < E) ? ((uint64_t)ordered_key(ld_coh(Lr + e)) << 32) | (uint32_t)(E - 1 - e) : 0ull;
-      }
-      for (int jj = 0; jj < k; ++jj) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int q = 0; q < kMaxE / 64; ++q) best = key[q] > best ? key[q] : best;
-        uint64_t m = best;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-          const uint64_t o = __shfl_xor(m, off, 64);
-          m = o > m ? o : m;
-        }
-#pragma unroll
-        for (int q = 0; q < kMaxE / 64; ++q)
-          if (key[q] == m) key[q] = 0ull;
-        if (lane == 0) {
-          sm.u.r.ids[tt * k + jj] = E - 1 - (int)(uint32_t)(m & 0xffffffffu);
-          sm.u.r.wl[wave][jj] = key_value((uint32_t)(m >> 32));
-        }
-      }
-      // softmax over the kept logits, summed in slot order
-      if (lane == 0) {
-        const float l0 = sm.u.r.wl[wave][0];
-        float s = 0.f;
-        for (int jj = 0; jj < k; ++jj) {
-          const float z = expf(sm.u.r.wl[wave][jj] - l0);
-          sm.u.r.wl[wave][jj] = z;
-          s += z;
-        }
-        for (int jj = 0; jj < k; ++jj) {
-          st_coh(P.wts + (size_t)t * k + jj, sm.u.r.wl[wave][jj] / s);
-          st_coh(P.ids + (size_t)t * k + jj, sm.u.r.ids[tt * k + jj]);
-        }
-      }
-    }
+    for (int w = 0; w < kMaxChunkTokens / 32; ++w) sm.u.r.mask[e][w] = 0u;
   }
-  // histogram of the chunk (integer counts; order-independent)
-  for (int e = tid; e < E; e += kThreads) sm.u.r.hist[e] = 0;
   __syncthreads();
   for (int q = tid; q < ntok * k; q += kThreads) {
     const int e = sm.u.r.ids[q];
-    if (e >= 0 && e < E) atomicAdd(&sm.u.r.hist[e], 1);
-    else __hip_atomic_store(P.ctrl + kSlotInts * C_ERR, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (e >= 0 && e < E) {
+      const int tt = q / k;
+      atomicAdd(&sm.u.r.hist[e], 1);
+      atomicOr(&sm.u.r.mask[e][tt >> 5], 1u << (tt & 31));
+    } else {
+      __hip_atomic_store(P.ctrl + kSlotInts * C_ERR, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kThreads) st_coh(P.hist + (size_t)c * E + e, sm.u.r.hist[e]);
-  const int old = wg_signal(P.ctrl + kSlotInts * C_KDONE);
-  if (tid == 0) sm.bcast[2] = (old == P.n_kc - 1) ? 1 : 0;
-  __syncthreads();
-  if (uni(sm.bcast[2]) && (P.phases & PH_PERMUTE)) plan_wg(P, sm);
 }
 
-// stable scatter of chunk c: position of slot (t, j) with expert e is
-//   offsets[e] + (slots of e in earlier chunks) + (slots of e in earlier tokens of this chunk)
+// stable scatter of a chunk: slot (t, j) with expert e goes to
+//   offsets[e] + base[e] + #(earlier tokens of the chunk that chose e)
+// (a token chooses an expert at most once, so the rank is a popcount of the mask)
 template <class SM>
-__device__ void scatter_item(const KParams &P, int c, SM &sm) {
-  const int tid = otid();
-  const int t0 = c * P.tk, ntok = min(P.tk, P.T - t0), k = P.k, E = P.E;
-  const int nq = ntok * k;
-  for (int q = tid; q < nq; q += kThreads) sm.u.r.ids[q] = ld_coh(P.ids + (size_t)t0 * k + q);
-  __syncthreads();
-  for (int q = tid; q < nq; q += kThreads) {
+__device__ __forceinline__ void chunk_scatter(const KParams &P, int c, int ntok, const int *offs, const int *base,
+                                              SM &sm) {
+  const int tid = otid(), k = P.k, E = P.E, t0 = c * P.tk;
+  for (int q = tid; q < ntok * k; q += kThreads) {
     const int e = sm.u.r.ids[q];
     if (e < 0 || e >= E) continue;
-    const int first = (q / k) * k;
+    const int tt = q / k;
     int rank = 0;
-    for (int q2 = 0; q2 < first; ++q2) rank += (sm.u.r.ids[q2] == e) ? 1 : 0;
-    const int p = ld_coh(P.offsets + e) + ld_coh(P.hist + (size_t)c * E + e) + rank;
+#pragma unroll
+    for (int w = 0; w < kMaxChunkTokens / 32; ++w) {
+      const uint32_t mw = sm.u.r.mask[e][w];
+      if (w < (tt >> 5)) rank += __popc(mw);
+      else if (w == (tt >> 5)) rank += __popc(mw & ((1u << (tt & 31)) - 1u));
+    }
+    const int p = offs[e] + (base ? base[e] : 0) + rank;
     const int slot = t0 * k + q;
     st_coh(P.perm + p, slot);
     st_coh(P.inv_perm + slot, p);
   }
+}
+
+// top-k of one token on one wave: NQ keys per lane (experts lane, lane + 64, ...), key =
+// (ordered logit << 32) | (E - 1 - expert), so the wave maximum is the largest logit with
+// ties to the lower id.  Writes the ids to ids_lds[0..k) and the gate weights (softmax of
+// the kept logits, summed in slot order) and ids to global memory.
+template <int NQ>
+__device__ __forceinline__ void topk_token(const KParams &P, int t, uint64_t (&key)[NQ], int *ids_lds) {
+  const int lane = otid() & 63, k = P.k, E = P.E;
+  float lj = 0.f;  // lane j keeps the logit and id of slot j (k <= 64)
+  int ej = 0;
+  for (int jj = 0; jj < k; ++jj) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) best = key[q] > best ? key[q] : best;
+    const uint64_t m = wave_max_u64(best);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      if (key[q] == m) key[q] = 0ull;
+    const int e = E - 1 - (int)(uint32_t)(m & 0xffffffffu);
+    if (lane == (jj & 63)) {
+      lj = key_value((uint32_t)(m >> 32));
+      ej = e;
+    }
+    if (lane == 0) ids_lds[jj] = e;
+  }
+  if (k <= 64) {
+    const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj), 0));
+    const float z = lane < k ? expf(lj - l0) : 0.f;
+    float ssum = 0.f;
+    for (int jj = 0; jj < k; ++jj) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), jj));
+    if (lane < k) {
+      st_coh(P.wts + (size_t)t * k + lane, z / ssum);
+      st_coh(P.ids + (size_t)t * k + lane, ej);
+    }
+  } else if (lane == 0) {
+    // k > 64: the kept logits again from memory (the same values, -0.0 read as +0.0)
+    const float *Lr = P.logits + (size_t)t * E;
+    const float l0 = ld_coh(Lr + ids_lds[0]) + 0.0f;
+    float ssum = 0.f;
+    for (int jj = 0; jj < k; ++jj) ssum += expf((ld_coh(Lr + ids_lds[jj]) + 0.0f) - l0);
+    for (int jj = 0; jj < k; ++jj) {
+      const int e = ids_lds[jj];
+      st_coh(P.wts + (size_t)t * k + jj, expf((ld_coh(Lr + e) + 0.0f) - l0) / ssum);
+      st_coh(P.ids + (size_t)t * k + jj, e);
+    }
+  }
+}
+
+// top-k + softmax for the kTopkTokens tokens of item c (one token per wave at a time);
+// for E <= 256 all of a wave's token logits are loaded before the first selection
+template <class SM>
+__device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, SM &sm) {
+  const int tid = otid(), wave = tid >> 6, lane = tid & 63, k = P.k, E = P.E;
+  if (E <= 256) {
+    constexpr int TPW = kTopkTokens / kWaves;  // tokens per wave
+    uint64_t key[TPW][4];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tt = wave + u * kWaves;
+      const float *Lr = P.logits + (size_t)(t0 + min(tt, ntok - 1)) * E;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = q * 64 + lane;
+        key[u][q] = e < E ? ((uint64_t)ordered_key(ld_coh(Lr + e)) << 32) | (uint32_t)(E - 1 - e) : 0ull;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tt = wave + u * kWaves;
+      if (tt < ntok) topk_token<4>(P, t0 + tt, key[u], sm.u.r.ids + tt * k);
+    }
+  } else {
+    for (int tt = wave; tt < ntok; tt += kWaves) {
+      const float *Lr = P.logits + (size_t)(t0 + tt) * E;
+      uint64_t key[kMaxE / 64];
+#pragma unroll
+      for (int q = 0; q < kMaxE / 64; ++q) {
+        const int e = q * 64 + lane;
+        key[q] = e < E ? ((uint64_t)ordered_key(ld_coh(Lr + e)) << 32) | (uint32_t)(E - 1 - e) : 0ull;
+      }
+      topk_token<kMaxE / 64>(P, t0 + tt, key, sm.u.r.ids + tt * k);
+    }
+  }
+}
+
+// K item c: top-k of kTopkTokens tokens.  With a single K item (T <= kTopkTokens) the same
+// workgroup builds the plan and scatters; otherwise it adds its per-expert counts to its
+// chunk's histogram (integer atomics: order-independent) and the last K item plans.
+template <class SM>
+__device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
+  const int tid = otid(), k = P.k, E = P.E;
+  const int t0 = c * kTopkTokens, ntok = min(kTopkTokens, P.T - t0);
+  if (P.phases & PH_IDS_GIVEN) {
+    for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = P.ids[(size_t)t0 * k + q];  // caller's input
+  } else {
+    topk_tokens(P, t0, ntok, sm);
+  }
+  __syncthreads();
+  if (!(P.phases & PH_PERMUTE)) {
+    wg_signal(P.ctrl + kSlotInts * C_KDONE);
+    return;
+  }
+  chunk_masks(P, ntok, sm);
+  if (P.n_kt == 1) {
+    plan_wg(P, sm, true);
+    __syncthreads();
+    chunk_scatter(P, 0, ntok, sm.u.r.scan0, nullptr, sm);
+    wg_signal(P.ctrl + kSlotInts * C_KDONE);
+    if (otid() == 0) __hip_atomic_fetch_add(P.ctrl + kSlotInts * C_PLAN, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (P.tk % kTopkTokens == 0) {  // the item lies in one chunk: add its histogram
+    const int chunk = t0 / P.tk;
+    for (int e = tid; e < E; e += kThreads) {
+      const int h = sm.u.r.hist[e];
+      if (h) __hip_atomic_fetch_add(P.hist + (size_t)chunk * E + e, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {  // large k: small chunks, one increment per slot
+    for (int q = tid; q < ntok * k; q += kThreads) {
+      const int e = sm.u.r.ids[q];
+      if (e >= 0 && e < E)
+        __hip_atomic_fetch_add(P.hist + (size_t)((t0 + q / k) / P.tk) * E + e, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const int old = wg_signal(P.ctrl + kSlotInts * C_KDONE);
+  if (tid == 0) sm.bcast[2] = (old == P.n_kt - 1) ? 1 : 0;
+  __syncthreads();
+  if (uni(sm.bcast[2])) {
+    plan_wg(P, sm, false);
+    wg_signal(P.ctrl + kSlotInts * C_PLAN);
+  }
+}
+
+// scatter of chunk c (several chunks): rebuild the chunk's masks from its ids
+template <class SM>
+__device__ __forceinline__ void scatter_item(const KParams &P, int c, SM &sm) {
+  const int tid = otid(), k = P.k, E = P.E;
+  const int t0 = c * P.tk, ntok = min(P.tk, P.T - t0);
+  for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = ld_coh(P.ids + (size_t)t0 * k + q);
+  __syncthreads();
+  chunk_masks(P, ntok, sm);
+  for (int e = tid; e < E; e += kThreads) {
+    sm.u.r.scan0[e] = ld_coh(P.offsets + e);
+    sm.u.r.scan1[e] = ld_coh(P.hist + (size_t)c * E + e);
+  }
+  __syncthreads();
+  chunk_scatter(P, c, ntok, sm.u.r.scan0, sm.u.r.scan1, sm);
 }
 
 template <int WT> struct ActT { using type = uint16_t; };
@@ -668,8 +915,10 @@ __device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i
   }
   f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
+  if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
   C::template run<false>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, sm.u.act, P.d,
                          ngroups);
+  if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
 #pragma unroll
   for (int b = 0; b < MG; ++b) {
     const int r = b * 16 + j;
@@ -729,8 +978,10 @@ __device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm) {
   }
   f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
+  if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
   C::template run<true>(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n * asz, sm.rows, sm.u.act, P.n,
                         ngroups);
+  if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
 #pragma unroll
   for (int b = 0; b < MG; ++b) {
     const int r = b * 16 + j;
@@ -806,7 +1057,7 @@ enum ItemKind : int { K_ZERO = 0, K_ROUTER = 1, K_TOPK = 2, K_SHGU = 3, K_SCATTE
 
 // register budget per kernel (waves per SIMD): 2 for the narrow tiles, 1 for the widest
 template <int WT, int MG> struct Occ {
-  static constexpr int waves = (MG == 8 || (MG == 4 && WT != WBF16)) ? 1 : 2;
+  static constexpr int waves = MG == 1 ? (WT == WFP8 ? 2 : 3) : (MG == 8 || (MG == 4 && WT != WBF16)) ? 1 : 2;
 };
 
 template <int WT, int MG>
@@ -820,11 +1071,7 @@ void moe_persistent(KParams P) {
     if (tid == 0) __hip_atomic_store(err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  const int n_Z = (P.phases & PH_FFN) ? P.n_zero : 0;
-  const int n_L = (P.phases & PH_ROUTE) ? P.n_lt * P.n_le : 0;
-  const int n_K = (P.phases & (PH_ROUTE | PH_PERMUTE)) ? P.n_kc : 0;
-  const int n_SG = (P.phases & PH_FFN) ? P.n_shmt * P.nt_gu : 0;
-  const int n_S = (P.phases & PH_PERMUTE) ? P.n_kc : 0;
+  const int n_Z = P.n_Z, n_L = P.n_L, n_K = P.n_K, n_SG = P.n_SG, n_S = P.n_S;
   const bool dyn = (P.phases & (PH_FFN | PH_COMBINE)) != 0;
   bool zero_seen = false, logits_seen = false, plan_seen = false, scat_seen = false, dn_seen = false;
   int n_mt = -1;
@@ -843,6 +1090,7 @@ void moe_persistent(KParams P) {
     // prefetch the next ticket; its value is read at the top of the next iteration
     if (dynamic && tid == 0) next = __hip_atomic_fetch_add(ctrl + kSlotInts * C_TICKET, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t t_start = P.trace ? wall_clock64() : 0;
+    if (P.trace && tid == 0) sm.mark[0] = sm.mark[1] = 0;
     int kind = -1;
     int i = ticket;
     if (i < n_Z) {
@@ -850,13 +1098,18 @@ void moe_persistent(KParams P) {
       wg_signal(ctrl + kSlotInts * C_ZDONE);
       kind = K_ZERO;
     } else if ((i -= n_Z) < n_L) {
-      logits_item<WT>(P, i, sm);
+      if constexpr (MG == 1) logits_item_split<WT>(P, i, sm);
+      else logits_item_tile<WT, MG>(P, i, sm);
       wg_signal(ctrl + kSlotInts * C_LDONE);
       kind = K_ROUTER;
     } else if ((i -= n_L) < n_K) {
       if (!(P.phases & PH_IDS_GIVEN) && !logits_seen) {
         if (!wg_wait(ctrl + kSlotInts * C_LDONE, n_L, err, sm)) break;
         logits_seen = true;
+      }
+      if (!zero_seen) {  // chunk histograms are cleared by the Z items
+        if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
+        zero_seen = true;
       }
       topk_item(P, i, sm);
       kind = K_TOPK;
@@ -918,7 +1171,11 @@ void moe_persistent(KParams P) {
       unsigned long long *rec = P.trace + 4 * (size_t)ticket;
       rec[0] = t_start;
       rec[1] = wall_clock64();
-      rec[2] = (unsigned long long)ticket;
+      // ticket | tile-loop start and end (16-bit offsets from the item start, 10 ns units)
+      const uint32_t m0 = sm.mark[0], m1 = sm.mark[1];
+      const unsigned long long d0 = m0 ? min((uint32_t)(m0 - (uint32_t)t_start), 0xffffu) : 0;
+      const unsigned long long d1 = m1 ? min((uint32_t)(m1 - (uint32_t)t_start), 0xffffu) : 0;
+      rec[2] = (unsigned long long)(uint32_t)ticket | (d0 << 32) | (d1 << 48);
       rec[3] = ((unsigned long long)blockIdx.x << 32) | (unsigned)kind;
     }
   }
@@ -1037,12 +1294,12 @@ moe_status launch(const Call &c) {
   P.dn_cols = L.tiles.dn_cols;
   P.n_lt = L.n_lt;
   P.n_le = L.n_le;
+  P.n_kt = L.n_kt;
   P.n_kc = L.n_kc;
   P.n_shmt = L.n_shmt;
   P.nt_gu = L.nt_gu;
   P.nt_dn = L.nt_dn;
   P.n_comb = L.n_comb;
-  P.n_zero = L.n_zero;
   P.mt_cap = L.mt_routed_max + L.n_shmt;
   P.x = c.hidden;
   P.wr = c.w_router;
@@ -1081,17 +1338,16 @@ moe_status launch(const Call &c) {
     P.trace_cap = c.opts->trace_bytes / 32;
   }
 
-  int n_items = 0;
-  {
-    const int n_Z = (P.phases & PH_FFN) ? P.n_zero : 0;
-    const int n_L = (P.phases & PH_ROUTE) ? P.n_lt * P.n_le : 0;
-    const int n_K = (P.phases & (PH_ROUTE | PH_PERMUTE)) ? P.n_kc : 0;
-    const int n_SG = (P.phases & PH_FFN) ? P.n_shmt * P.nt_gu : 0;
-    const int n_S = (P.phases & PH_PERMUTE) ? P.n_kc : 0;
-    n_items = n_Z + n_L + n_K + n_SG + n_S;
-    if (P.phases & PH_FFN)
-      n_items += L.mt_routed_max * (P.nt_gu + P.nt_dn) + P.n_shmt * P.nt_dn + P.n_comb;
-  }
+  const PhaseCounts pc = phase_counts(L, P.phases);
+  P.n_Z = pc.z;
+  P.n_L = pc.l;
+  P.n_K = pc.k;
+  P.n_SG = pc.sg;
+  P.n_S = pc.s;
+  P.gd_words = pc.gd_words;
+  P.hist_words = pc.hist_words;
+  int n_items = pc.z + pc.l + pc.k + pc.sg + pc.s;
+  if (P.phases & PH_FFN) n_items += L.mt_routed_max * (P.nt_gu + P.nt_dn) + P.n_shmt * P.nt_dn + P.n_comb;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;

@@ -19,8 +19,9 @@ constexpr int kSlotInts = 1024;        // control slots sit 4 KB apart (separate
 constexpr int kCtrlBytes = 16 * kSlotInts * 4;  // control block at the start of the workspace
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 256;
-constexpr int kLogitTokens = 16;       // router item: 16 tokens x 16 experts, K split over 4 waves
-constexpr int kLogitExperts = 16;
+constexpr int kTopkTokens = 16;        // tokens per top-k item (4 per wave)
+constexpr int kMaxChunkTokens = 128;   // tokens per scatter chunk (rank bitmasks: 4 words)
+constexpr int kMaxChunkSlots = 1024;   // (token, slot) pairs per chunk
 constexpr int kCombineTokens = 1;      // combine item: 1 token
 constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroing item
 
@@ -41,19 +42,22 @@ struct Tiles {
   int nf;          // 16-row weight fragments per wave (2 when mg == 1, else 4)
   int gu_cols;     // H columns per gate/up item: 4 waves x nf/2 x 16
   int dn_cols;     // output columns per down item: 4 waves x nf x 16
-  int tk;          // tokens per top-k / scatter chunk (tk * k <= 256)
+  int tk;          // tokens per scatter chunk (tk <= 128, tk * k <= 1024)
+  int rt_tokens;   // router item: tokens x experts (16 x 16 split over the 4 waves when
+  int rt_experts;  //   mg == 1, else min(bm, 64) x 64*nf on the expert tile core)
 };
 
 struct Layout {
   Tiles tiles;
   int64_t T;
+  int E;
   int n_lt, n_le;        // router items: token tiles x expert blocks
-  int n_kc;              // top-k / scatter chunks
+  int n_kt;              // top-k items (kTopkTokens tokens each)
+  int n_kc;              // scatter chunks
   int mt_routed_max;     // bound on routed m-tiles
   int n_shmt;            // shared-expert m-tiles
   int nt_gu, nt_dn;      // gate/up and down items per m-tile
   int n_comb;            // combine items
-  int n_zero;            // counter-clearing items
   int64_t rows_h;        // rows of H and Y: T*k + n_shared*T
   // byte offsets into the workspace
   size_t off_gudone, off_desc, off_logits, off_ids, off_wts, off_hist, off_counts, off_offsets, off_mtoff,
@@ -95,20 +99,33 @@ inline Tiles choose_tiles(const moe_problem *p) {
   t.nf = t.mg == 1 ? 2 : 4;
   t.gu_cols = 4 * (t.nf / 2) * 16;
   t.dn_cols = 4 * t.nf * 16;
-  t.tk = 256 / p->k;
+  t.tk = kMaxChunkSlots / p->k;
+  if (t.tk > kMaxChunkTokens) t.tk = kMaxChunkTokens;
   if (t.tk < 1) t.tk = 1;
+  t.rt_tokens = 16 * (t.mg > 4 ? 4 : t.mg);
+  t.rt_experts = t.mg == 1 ? 16 : 64 * t.nf;
   return t;
 }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Work items of one launch, per phase, in ticket order: Z (clear counters), L (router),
+// K (top-k), SG (shared gate/up), S (scatter); the routed gate/up, down and combine items
+// follow and are counted on the device once the plan exists.
+struct PhaseCounts {
+  int gd_words, hist_words;  // words cleared by Z items: dependency counters, chunk histograms
+  int z, l, k, sg, s;
+};
 
 inline Layout make_layout(const moe_problem *p) {
   Layout L{};
   L.tiles = choose_tiles(p);
   const int64_t T = p->T, k = p->k, E = p->E, bm = L.tiles.bm;
   L.T = T;
-  L.n_lt = (int)ceil_div(T, kLogitTokens);
-  L.n_le = (int)ceil_div(E, kLogitExperts);
+  L.E = (int)E;
+  L.n_lt = (int)ceil_div(T, L.tiles.rt_tokens);
+  L.n_le = (int)ceil_div(E, L.tiles.rt_experts);
+  L.n_kt = (int)ceil_div(T, kTopkTokens);
   L.n_kc = (int)ceil_div(T, L.tiles.tk);
   const int64_t tk = T * k;
   int64_t bound = tk / bm + (E < tk ? E : tk);
@@ -118,7 +135,6 @@ inline Layout make_layout(const moe_problem *p) {
   L.nt_gu = p->n / L.tiles.gu_cols;
   L.nt_dn = (int)ceil_div(p->d, L.tiles.dn_cols);
   L.n_comb = (int)ceil_div(T, kCombineTokens);
-  L.n_zero = (int)ceil_div(L.mt_routed_max + L.n_shmt, kZeroPerItem);
   L.rows_h = tk + (int64_t)p->n_shared * T;
   const size_t asz = dtype_size(p->act_dtype);
   size_t o = kCtrlBytes;
@@ -142,6 +158,20 @@ inline Layout make_layout(const moe_problem *p) {
   L.off_y = take(asz * (size_t)L.rows_h * (size_t)p->d);
   L.total = o;
   return L;
+}
+
+inline PhaseCounts phase_counts(const Layout &L, int phases) {
+  PhaseCounts c{};
+  const bool ffn = (phases & PH_FFN) != 0, perm = (phases & PH_PERMUTE) != 0;
+  const bool many = L.n_kt > 1;  // one top-k item plans and scatters by itself
+  c.gd_words = ffn ? L.mt_routed_max + L.n_shmt : 0;
+  c.hist_words = (perm && many) ? L.n_kc * L.E : 0;
+  c.z = (int)ceil_div(c.gd_words + c.hist_words, kZeroPerItem);
+  c.l = (phases & PH_ROUTE) ? L.n_lt * L.n_le : 0;
+  c.k = (phases & (PH_ROUTE | PH_PERMUTE)) ? L.n_kt : 0;
+  c.sg = ffn ? L.n_shmt * L.nt_gu : 0;
+  c.s = (perm && many) ? L.n_kc : 0;
+  return c;
 }
 
 }  // namespace moe

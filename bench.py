@@ -80,6 +80,32 @@ def algorithmic(cfg, counts, n_shared):
     return b, f, touched
 
 
+KERNEL_SOURCES = ("routed_grouped_gemm_amd/csrc/moe_kernels.hip", "routed_grouped_gemm_amd/csrc/moe_plan.h")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    sha = h.hexdigest()[:16]
+    path = os.path.join(ROOT, "profiles", f"moe_persistent_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    if fields.get("kernel_source_sha") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(inp, budget_s=12.0):
     """The oracle as it stands, on this host: whole forwards of the same workload
     (or its first tokens, for the large configs) repeated within a time budget."""
@@ -186,7 +212,11 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tfl, 2), "peak": peak_mfma, "unit": "TFLOP/s",
                 "frac": round(tfl / peak_mfma, 4)}
-    roof["traffic"] = None
+    traffic = measured_traffic(cfg["name"])
+    roof["traffic"] = traffic
+    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1)"
+    if traffic:
+        roof["traffic_over_algorithmic"] = round(traffic / B, 3)
     roof["bytes_per_launch"] = int(B)
     roof["flops_per_launch"] = int(F)
     roof["kernel"] = "moe_persistent"

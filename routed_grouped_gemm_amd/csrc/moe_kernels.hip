@@ -47,6 +47,12 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// 16-byte streaming (nontemporal) load from global memory; the explicit address space keeps
+// it a global_load even when the address comes from a select with a uniform value
+__device__ __forceinline__ uint4 ld_stream16(const void *p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)p));
+}
+
 enum : int { WF32 = 0, WBF16 = 1, WFP8 = 2 };
 
 // KU: K elements per 16-byte weight load of one lane; WSZ/ASZ: weight/activation bytes
@@ -61,8 +67,12 @@ template <int WT, int MG> struct Shape {
   static constexpr int NF = MG == 1 ? 2 : 4;
   // register/LDS buffers: three (two K chunks in flight) where the registers allow it,
   // else two (one chunk in flight, longer chunks)
-  static constexpr int NBUF = (MG == 1 || (MG == 2 && WT != WFP8)) ? 3 : 2;
-  static constexpr int FL = WT == WFP8 ? 2 : (MG == 1 || NBUF == 2) ? 4 : 2;
+#ifndef MOE_NBUF
+#define MOE_NBUF(WT, MG) ((MG == 2 && WT == WFP8) ? 2 : 3)
+#define MOE_FL(WT, MG) ((WT != WFP8 && MG == 1) ? 4 : 2)
+#endif
+  static constexpr int NBUF = MOE_NBUF(WT, MG);
+  static constexpr int FL = MOE_FL(WT, MG);
 };
 
 struct KParams {
@@ -95,10 +105,21 @@ struct KParams {
 // small helpers
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v) |
+         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)) << 32);
+}
 
 // otid() behind an empty volatile asm: values derived from it are recomputed in each
 // work item instead of being hoisted out of the persistent loop (where they would stay
 // live, in registers, across every item)
+// p, passed through an empty volatile asm: what it points to is unknown to the compiler
+// afterwards, so loads through it stay ordered with memory-clobbering asm statements
+__device__ __forceinline__ const char *laundered(const char *p) {
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
 __device__ __forceinline__ int otid() {
   int t = threadIdx.x;
   asm volatile("" : "+v"(t));
@@ -110,16 +131,47 @@ __device__ __forceinline__ int otid() {
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");  // memory accesses stay on their side of the wait
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ void wait_vm0() { wait_vm<0>(); }
 
+// Workgroup barrier without the fences of __syncthreads.  Those fences wait for every
+// outstanding vector memory operation (the LDS DMA counts as one), which would drain the
+// prefetch pipeline at every K chunk.  The caller has already waited for the LDS data the
+// barrier publishes; the empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// The activation staging buffers are three separate LDS variables: the compiler can then
+// tell that a read of one buffer does not depend on a DMA still filling another, and does
+// not wait for the prefetches before every LDS read.
+struct Lds3 {
+  char *b0, *b1, *b2;
+};
+
 // 16 bytes per lane, global -> LDS; lane l lands at lds_base + 16*l (lds_base uniform).
 // COH selects the device-coherent cache policy (SC1) for data written in this launch.
+// Written as inline assembly on purpose: the compiler tracks the builtin form as an
+// asynchronous LDS write and then makes every later LDS read wait for all outstanding
+// vector memory operations (prefetches included), which serialises the K pipeline.  Here
+// the waits are explicit instead: a chunk's DMA is complete once the issuing wave has
+// waited for it (vmcnt) and passed the workgroup barrier.  No VGPR is written, so no
+// register can be reused under an in-flight load; M0 is bound through its constraint.
 template <bool COH>
 __device__ __forceinline__ void dma16(const void *g, void *lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                   (__attribute__((address_space(3))) void *)lds_base, 16, 0, COH ? 16 : 0);
+  const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)reinterpret_cast<uintptr_t>(lds_base));
+  if constexpr (COH)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" ::"v"(g), "{m0}"(m0v) : "memory");
+  else
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
 }
 
 __device__ __forceinline__ int ld_relaxed(const int *p) {
@@ -132,19 +184,30 @@ __device__ __forceinline__ int ld_relaxed(const int *p) {
 // then only waits for its stores to complete (s_waitcnt) before bumping a counter, and a
 // consumer reads after seeing the counter: no agent-scope fence, so no whole-L2 write-back
 // or invalidation on the hot path (those cost more than the work items themselves).
-__device__ __forceinline__ void st_coh(int *p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// (every pointer is cast to the global address space: the data always lives in device
+// memory, and a generic pointer would make these flat accesses, which the compiler has to
+// wait for conservatively)
+typedef __attribute__((address_space(1))) int gint;
+typedef __attribute__((address_space(1))) uint64_t gu64;
+__device__ __forceinline__ void st_coh(int *p, int v) { __hip_atomic_store((gint *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ void st_coh(float *p, float v) {
-  __hip_atomic_store(reinterpret_cast<int *>(p), __float_as_int(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((gint *)p, __float_as_int(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_coh64(void *p, uint64_t v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((gu64 *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int ld_coh(const int *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ int ld_coh(const int *p) {
+  return __hip_atomic_load((const gint *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ float ld_coh(const float *p) {
-  return __int_as_float(__hip_atomic_load(reinterpret_cast<const int *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return __int_as_float(__hip_atomic_load((const gint *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 __device__ __forceinline__ uint64_t ld_coh64(const void *p) {
-  return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((const gu64 *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// plain 16-byte global load (data not written during this launch)
+__device__ __forceinline__ uint4 ld_glob16(const void *p) {
+  return __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4 *)p);
 }
 __device__ __forceinline__ int4 ld_coh_int4(const int4 *p) {
   const uint64_t a = ld_coh64(p), b = ld_coh64(reinterpret_cast<const char *>(p) + 8);
@@ -248,11 +311,12 @@ template <int WT, int MG> struct Core {
   static constexpr int NCOL = RB / 16;          // 16-byte columns per row
   static constexpr int BMR = MG * 16;
   static constexpr int RPK = 1024 / RB;         // rows per 1 KB load-to-LDS block
-  static constexpr int NDMA = BMR * RB / 1024 / kWaves;
+  static constexpr int NKB = BMR * RB / 1024;             // 1 KB load-to-LDS blocks per chunk
+  static constexpr int NDMA = NKB >= kWaves ? NKB / kWaves : 1;  // per wave (waves >= NKB: none)
   static constexpr int BUF = BMR * RB;          // bytes of one LDS buffer
   static constexpr int NBUF = Shape<WT, MG>::NBUF;
   static constexpr int PER_CHUNK = NDMA + NF * FL;  // vector memory ops per wave per chunk
-  static_assert(NDMA >= 1 && RPK >= 1, "tile shape");
+  static_assert(NKB >= 1 && RPK >= 1 && (NKB < kWaves || NKB % kWaves == 0), "tile shape");
 
   // the MFMAs of one K chunk; FULL: every token group is present (no per-group branch,
   // so LDS reads and MFMAs of different groups interleave freely)
@@ -318,7 +382,8 @@ template <int WT, int MG> struct Core {
   // with the device-coherent policy
   template <bool COH>
   __device__ static void run(f4 (&acc)[NF][MG], const char *const (&wrow)[NF], const float *const (&sc)[NF],
-                             const char *abase, size_t arow_bytes, const int *rows, char *lds, int K, int ngroups) {
+                             const char *abase, size_t arow_bytes, const int *rows, const Lds3 &lb, int K,
+                             int ngroups) {
     const int tid = otid(), lane = tid & 63, g = lane >> 4, j = lane & 15;
     const int wv = uni(tid >> 6);
     const int nch = K / KC;
@@ -331,105 +396,114 @@ template <int WT, int MG> struct Core {
 #pragma unroll
     for (int s = 0; s < NDMA; ++s) {
       const int q = s * kWaves + wv;
-      const int r = q * RPK + lane / NCOL;
+      const int r = min(q * RPK + lane / NCOL, BMR - 1);  // (clamped for waves without DMA)
       const int col = (lane % NCOL) ^ (r & (NCOL - 1));
       asrc[s] = abase + (size_t)rows[r] * arow_bytes + col * 16;
     }
-    auto dma = [&](int c, int buf) {
+    // Prefetches past the last chunk still issue, from one fixed address (a single cache
+    // line for the whole wave), so every pipeline stage has the same memory operations:
+    // the wait counts stay constant and the compiler's register scoreboard stays exact
+    // across the loop's back edge (a conditional prefetch makes it wait for everything).
+    // The weight pointers are laundered through empty asm: the compiler can then no longer
+    // prove the weights unchanging, so it keeps each prefetch between the barriers (memory
+    // clobbers) of its own pipeline stage instead of moving it across stages, which would
+    // break the per-stage wait counts.
+    const char *wr[NF];
 #pragma unroll
-      for (int s = 0; s < NDMA; ++s) dma16<COH>(asrc[s] + (size_t)c * RB, lds + buf * BUF + (s * kWaves + wv) * 1024);
+    for (int a = 0; a < NF; ++a) wr[a] = laundered(wrow[a]);
+    const char *adummy = reinterpret_cast<const char *>(uni64(reinterpret_cast<uint64_t>(abase)));
+    const char *wdummy = reinterpret_cast<const char *>(uni64(reinterpret_cast<uint64_t>(wr[0])));
+    auto dma = [&](int c, char *buf) {
+      const bool real = c < nch;
+      if (NKB >= kWaves || wv < NKB) {
+#pragma unroll
+        for (int s = 0; s < NDMA; ++s)
+          dma16<COH>(real ? asrc[s] + (size_t)c * RB : adummy, buf + (s * kWaves + wv) * 1024);
+      }
     };
     auto ldw = [&](uint4(&W)[NF][FL], int c) {
+      const bool real = c < nch;
 #pragma unroll
       for (int f = 0; f < FL; ++f)
 #pragma unroll
         for (int a = 0; a < NF; ++a)
-          W[a][f] = __builtin_bit_cast(
-              uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow[a] + (size_t)c * (FL * 64) + f * 64)));
+          W[a][f] = ld_stream16(real ? wr[a] + (size_t)c * (FL * 64) + f * 64 : wdummy);
     };
-    auto compute = [&](const uint4(&W)[NF][FL], int buf, int c) {
-      const char *A = lds + buf * BUF;
-      // small tiles compute every token group (rows past the tile's end repeat its last
-      // row, valid data whose results are not stored); large tiles skip absent groups,
-      // which also keeps the compiler from hoisting every LDS read of the chunk at once
+    // small tiles compute every token group (rows past the tile's end repeat its last
+    // row, valid data whose results are not stored); large tiles skip absent groups,
+    // which also keeps the compiler from hoisting every LDS read of the chunk at once
+    auto compute = [&](const uint4(&W)[NF][FL], const char *A, int c) {
+      asm volatile("" ::: "memory");  // the stage's prefetches are issued before its math
       chunk_mfma<(MG <= 2)>(acc, W, A, sc, c, ngroups, g, j);
     };
-
     if constexpr (NBUF == 2) {
-      // one chunk in flight: wait for everything, then issue the next chunk and compute
+      // one chunk in flight: wait for it, then issue the next one and compute
       uint4 wA[NF][FL], wB[NF][FL];
-      dma(0, 0);
+      dma(0, lb.b0);
       ldw(wA, 0);
-      for (int c = 0; c < nch; c += 2) {
+      for (int c = 0;; c += 2) {
         wait_vm0();
-        __syncthreads();
-        if (c + 1 < nch) {
-          dma(c + 1, 1);
-          ldw(wB, c + 1);
-        }
-        compute(wA, 0, c);
+        lds_barrier();
+        dma(c + 1, lb.b1);
+        ldw(wB, c + 1);
+        compute(wA, lb.b0, c);
         if (c + 1 >= nch) break;
         wait_vm0();
-        __syncthreads();
-        if (c + 2 < nch) {
-          dma(c + 2, 0);
-          ldw(wA, c + 2);
-        }
-        compute(wB, 1, c + 1);
+        lds_barrier();
+        dma(c + 2, lb.b0);
+        ldw(wA, c + 2);
+        compute(wB, lb.b1, c + 1);
+        if (c + 2 >= nch) break;
       }
     } else {
       // two chunks in flight: wait only for the oldest one (vmcnt counts this wave's
-      // outstanding operations in issue order), then refill the buffer freed by the
-      // previous step; the barrier also tells every wave that the LDS buffer about to be
-      // refilled has been read by all of them
+      // outstanding operations, which complete in issue order), then refill the buffer
+      // freed by the previous step; the barrier also tells every wave that the buffer about
+      // to be refilled has been read by all of them
       uint4 w0[NF][FL], w1[NF][FL], w2[NF][FL];
-      dma(0, 0);
+      dma(0, lb.b0);
       ldw(w0, 0);
-      if (nch > 1) {
-        dma(1, 1);
-        ldw(w1, 1);
-      }
-      for (int c = 0; c < nch; c += 3) {
-        if (c + 1 < nch) wait_vm<PER_CHUNK>(); else wait_vm0();
-        __syncthreads();
-        if (c + 2 < nch) {
-          dma(c + 2, 2);
-          ldw(w2, c + 2);
-        }
-        compute(w0, 0, c);
+      dma(1, lb.b1);
+      ldw(w1, 1);
+      for (int c = 0;; c += 3) {
+        wait_vm<PER_CHUNK>();
+        lds_barrier();
+        dma(c + 2, lb.b2);
+        ldw(w2, c + 2);
+        compute(w0, lb.b0, c);
         if (c + 1 >= nch) break;
-        if (c + 2 < nch) wait_vm<PER_CHUNK>(); else wait_vm0();
-        __syncthreads();
-        if (c + 3 < nch) {
-          dma(c + 3, 0);
-          ldw(w0, c + 3);
-        }
-        compute(w1, 1, c + 1);
+        wait_vm<PER_CHUNK>();
+        lds_barrier();
+        dma(c + 3, lb.b0);
+        ldw(w0, c + 3);
+        compute(w1, lb.b1, c + 1);
         if (c + 2 >= nch) break;
-        if (c + 3 < nch) wait_vm<PER_CHUNK>(); else wait_vm0();
-        __syncthreads();
-        if (c + 4 < nch) {
-          dma(c + 4, 1);
-          ldw(w1, c + 4);
-        }
-        compute(w2, 2, c + 2);
+        wait_vm<PER_CHUNK>();
+        lds_barrier();
+        dma(c + 4, lb.b1);
+        ldw(w1, c + 4);
+        compute(w2, lb.b2, c + 2);
+        if (c + 3 >= nch) break;
       }
     }
+    wait_vm0();  // the trailing prefetches land before the caller reuses the buffers
   }
 };
 
 // ---------------------------------------------------------------------------------
 // shared memory
 // ---------------------------------------------------------------------------------
+// bytes of each of the three activation staging buffers (separate LDS variables, see Lds3):
+// the expert tile's chunk, or the router tile's on kernels whose router uses the tile core
+template <int WT, int MG> struct ActBuf {
+  using RC = Core<(WT == WF32 ? WF32 : WBF16), 1>;
+  static constexpr int BYTES = (MG > 1 && RC::BUF > Core<WT, MG>::BUF) ? RC::BUF : Core<WT, MG>::BUF;
+};
+
 template <int WT, int MG> struct Smem {
-  static_assert(MG == 1 || Core<(WT == WF32 ? WF32 : WBF16), (MG > 4 ? 4 : MG)>::NBUF *
-                                   Core<(WT == WF32 ? WF32 : WBF16), (MG > 4 ? 4 : MG)>::BUF <=
-                               Core<WT, MG>::NBUF * Core<WT, MG>::BUF,
-                "router tile must fit the activation buffers");
   union {
-    char act[Core<WT, MG>::NBUF * Core<WT, MG>::BUF];
     struct {
-      int ids[kTopkTokens * kMaxK > kMaxChunkSlots ? kTopkTokens * kMaxK : kMaxChunkSlots];  // ids, slot order
+      int16_t ids[kTopkTokens * kMaxK > kMaxChunkSlots ? kTopkTokens * kMaxK : kMaxChunkSlots];  // ids (-1: invalid)
       int hist[kMaxE];                         // per-expert slot counts of the chunk
       int tmp[kMaxE];                          // per-expert m-tile counts (plan)
       int scan0[kMaxE + 1];                    // offsets (plan)
@@ -503,8 +577,10 @@ __device__ __forceinline__ void logits_item_split(const KParams &P, int i, SM &s
     for (int u = 0; u < 16; ++u)
       if (s0 + u < nsteps) acc = mfma_step<RT>(w[u], a[u], a[u], acc);
   }
+  if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
   sm.u.red[wv][lane] = acc;
   __syncthreads();
+  if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
   if (wv == 0) {
     const f4 sum = ((sm.u.red[0][lane] + sm.u.red[1][lane]) + sm.u.red[2][lane]) + sm.u.red[3][lane];
     const int t = t0 + j;
@@ -518,12 +594,12 @@ __device__ __forceinline__ void logits_item_split(const KParams &P, int i, SM &s
   }
 }
 
-// router logits, wide tiles: bm tokens x 64*NF experts on the expert tile core (router
-// rows are the weight operand, token rows the activation operand)
+// router logits, wide tiles: 16 tokens x 128 experts on the expert tile core (router rows
+// are the weight operand, token rows the activation operand)
 template <int WT, int MG, class SM>
-__device__ __forceinline__ void logits_item_tile(const KParams &P, int i, SM &sm) {
+__device__ __forceinline__ void logits_item_tile(const KParams &P, int i, SM &sm, const Lds3 &lb) {
   constexpr int RT = (WT == WF32) ? WF32 : WBF16;
-  constexpr int RMG = MG > 4 ? 4 : MG;  // at most 64 tokens per router tile (register budget)
+  constexpr int RMG = 1;  // 16 tokens x 128 experts: enough items to spread over the GPU
   using C = Core<RT, RMG>;
   constexpr int NF = C::NF;
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
@@ -542,7 +618,7 @@ __device__ __forceinline__ void logits_item_tile(const KParams &P, int i, SM &sm
     sc[a] = nullptr;
   }
   f4 acc[NF][RMG];
-  C::template run<false>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, sm.u.act, P.d,
+  C::template run<false>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, lb, P.d,
                          (m + 15) >> 4);
 #pragma unroll
   for (int a = 0; a < NF; ++a) {
@@ -578,30 +654,24 @@ __device__ __forceinline__ void wave_excl_scan(const int *in, int *out, int N, i
   if (lane == 63) out[N] = incl;
 }
 
-// max of a 64-bit key over the wave, in every lane: the row-shift / row-broadcast DPP
-// reduction (VALU data movement, no LDS round trips), result read from lane 63
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-#define MOE_DPP_MAX(CTRL, ROWM, BANKM)                                                      \
-  {                                                                                        \
-    const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWM, BANKM, false);    \
-    const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWM, BANKM, false);    \
-    const uint64_t o = ((uint64_t)ohi << 32) | olo, c = ((uint64_t)hi << 32) | lo;         \
-    if (o > c) {                                                                           \
-      lo = olo;                                                                            \
-      hi = ohi;                                                                            \
-    }                                                                                      \
+// wave-wide max (MAX) or min of a 32-bit value, returned in every lane: row-shift and
+// row-broadcast DPP steps (VALU data movement, no LDS round trips), result read from lane 63
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+#define MOE_DPP_RED(CTRL, ROWM, BANKM)                                              \
+  {                                                                                \
+    const uint32_t o = __builtin_amdgcn_update_dpp(v, v, CTRL, ROWM, BANKM, false); \
+    v = MAX ? (o > v ? o : v) : (o < v ? o : v);                                   \
   }
-  MOE_DPP_MAX(0x111, 0xf, 0xf)  // row_shr:1
-  MOE_DPP_MAX(0x112, 0xf, 0xf)  // row_shr:2
-  MOE_DPP_MAX(0x113, 0xf, 0xf)  // row_shr:3
-  MOE_DPP_MAX(0x114, 0xf, 0xe)  // row_shr:4
-  MOE_DPP_MAX(0x118, 0xf, 0xc)  // row_shr:8
-  MOE_DPP_MAX(0x142, 0xa, 0xf)  // row_bcast:15
-  MOE_DPP_MAX(0x143, 0xc, 0xf)  // row_bcast:31
-#undef MOE_DPP_MAX
-  const uint32_t rlo = __builtin_amdgcn_readlane(lo, 63), rhi = __builtin_amdgcn_readlane(hi, 63);
-  return ((uint64_t)rhi << 32) | rlo;
+  MOE_DPP_RED(0x111, 0xf, 0xf)  // row_shr:1
+  MOE_DPP_RED(0x112, 0xf, 0xf)  // row_shr:2
+  MOE_DPP_RED(0x113, 0xf, 0xf)  // row_shr:3
+  MOE_DPP_RED(0x114, 0xf, 0xe)  // row_shr:4
+  MOE_DPP_RED(0x118, 0xf, 0xc)  // row_shr:8
+  MOE_DPP_RED(0x142, 0xa, 0xf)  // row_bcast:15
+  MOE_DPP_RED(0x143, 0xc, 0xf)  // row_bcast:31
+#undef MOE_DPP_RED
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // The plan: counts -> offsets (exclusive scan), m-tile counts -> m-tile offsets, the
@@ -651,6 +721,9 @@ __device__ __forceinline__ void plan_wg(const KParams &P, SM &sm, bool from_lds)
   if (tid == 0) st_coh(P.ctrl + kSlotInts * C_NMT, smt[E]);
 }
 
+// an expert id as kept in LDS: out-of-range ids (caller input) become -1 and are reported
+__device__ __forceinline__ int16_t checked_id(int e, int E) { return (int16_t)((e >= 0 && e < E) ? e : -1); }
+
 // chunk histogram and per-expert token bitmasks from the chunk's ids in sm.u.r.ids
 template <class SM>
 __device__ __forceinline__ void chunk_masks(const KParams &P, int ntok, SM &sm) {
@@ -699,86 +772,122 @@ __device__ __forceinline__ void chunk_scatter(const KParams &P, int c, int ntok,
   }
 }
 
-// top-k of one token on one wave: NQ keys per lane (experts lane, lane + 64, ...), key =
-// (ordered logit << 32) | (E - 1 - expert), so the wave maximum is the largest logit with
-// ties to the lower id.  Writes the ids to ids_lds[0..k) and the gate weights (softmax of
-// the kept logits, summed in slot order) and ids to global memory.
-template <int NQ>
-__device__ __forceinline__ void topk_token(const KParams &P, int t, uint64_t (&key)[NQ], int *ids_lds) {
+// top-k of TPW tokens on one wave, in lockstep (their reductions are independent, so they
+// overlap).  Lane l holds the keys of experts l, l + 64, ... (NQ of them): the ordered
+// 32-bit image of the logit, 0 for absent or already taken experts.  Each round takes the
+// largest key (wave max), then the lowest expert id holding it (wave min), which is the
+// (logit descending, id ascending) order.  Slot j's id and logit stay in lane j (k <= 64);
+// the gate weights are the softmax of the kept logits, summed in slot order.
+template <int NQ, int TPW>
+__device__ __forceinline__ void topk_group(const KParams &P, const int (&t)[TPW], const bool (&live)[TPW],
+                                           uint32_t (&key)[TPW][NQ], int16_t *const (&ids_lds)[TPW]) {
   const int lane = otid() & 63, k = P.k, E = P.E;
-  float lj = 0.f;  // lane j keeps the logit and id of slot j (k <= 64)
-  int ej = 0;
-  for (int jj = 0; jj < k; ++jj) {
-    uint64_t best = 0;
+  float lj[TPW];
+  int ej[TPW];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) best = key[q] > best ? key[q] : best;
-    const uint64_t m = wave_max_u64(best);
-#pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      if (key[q] == m) key[q] = 0ull;
-    const int e = E - 1 - (int)(uint32_t)(m & 0xffffffffu);
-    if (lane == (jj & 63)) {
-      lj = key_value((uint32_t)(m >> 32));
-      ej = e;
-    }
-    if (lane == 0) ids_lds[jj] = e;
+  for (int u = 0; u < TPW; ++u) {
+    lj[u] = 0.f;
+    ej[u] = 0;
   }
-  if (k <= 64) {
-    const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj), 0));
-    const float z = lane < k ? expf(lj - l0) : 0.f;
-    float ssum = 0.f;
-    for (int jj = 0; jj < k; ++jj) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), jj));
-    if (lane < k) {
-      st_coh(P.wts + (size_t)t * k + lane, z / ssum);
-      st_coh(P.ids + (size_t)t * k + lane, ej);
+  for (int jj = 0; jj < k; ++jj) {
+    uint32_t m[TPW], c[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      uint32_t b = key[u][0];
+#pragma unroll
+      for (int q = 1; q < NQ; ++q) b = key[u][q] > b ? key[u][q] : b;
+      m[u] = wave_reduce_u32<true>(b);
     }
-  } else if (lane == 0) {
-    // k > 64: the kept logits again from memory (the same values, -0.0 read as +0.0)
-    const float *Lr = P.logits + (size_t)t * E;
-    const float l0 = ld_coh(Lr + ids_lds[0]) + 0.0f;
-    float ssum = 0.f;
-    for (int jj = 0; jj < k; ++jj) ssum += expf((ld_coh(Lr + ids_lds[jj]) + 0.0f) - l0);
-    for (int jj = 0; jj < k; ++jj) {
-      const int e = ids_lds[jj];
-      st_coh(P.wts + (size_t)t * k + jj, expf((ld_coh(Lr + e) + 0.0f) - l0) / ssum);
-      st_coh(P.ids + (size_t)t * k + jj, e);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      uint32_t x = 0xffffffffu;
+#pragma unroll
+      for (int q = NQ - 1; q >= 0; --q)
+        if (key[u][q] == m[u]) x = (uint32_t)(q * 64 + lane);  // the lowest matching id of this lane
+      c[u] = wave_reduce_u32<false>(x);
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if ((uint32_t)(q * 64 + lane) == c[u]) key[u][q] = 0u;
+      if (lane == (jj & 63)) {
+        lj[u] = key_value(m[u]);
+        ej[u] = (int)c[u];
+      }
+      if (lane == 0 && live[u]) ids_lds[u][jj] = (int16_t)c[u];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    if (!live[u]) continue;
+    if (k <= 64) {
+      const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj[u]), 0));
+      const float z = lane < k ? expf(lj[u] - l0) : 0.f;
+      float ssum = 0.f;
+      for (int jj = 0; jj < k; ++jj) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), jj));
+      if (lane < k) {
+        st_coh(P.wts + (size_t)t[u] * k + lane, z / ssum);
+        st_coh(P.ids + (size_t)t[u] * k + lane, ej[u]);
+      }
+    } else if (lane == 0) {
+      // k > 64: the kept logits again from memory (the same values, -0.0 read as +0.0)
+      const float *Lr = P.logits + (size_t)t[u] * E;
+      const float l0 = ld_coh(Lr + ids_lds[u][0]) + 0.0f;
+      float ssum = 0.f;
+      for (int jj = 0; jj < k; ++jj) ssum += expf((ld_coh(Lr + ids_lds[u][jj]) + 0.0f) - l0);
+      for (int jj = 0; jj < k; ++jj) {
+        const int e = ids_lds[u][jj];
+        st_coh(P.wts + (size_t)t[u] * k + jj, expf((ld_coh(Lr + e) + 0.0f) - l0) / ssum);
+        st_coh(P.ids + (size_t)t[u] * k + jj, e);
+      }
     }
   }
 }
 
-// top-k + softmax for the kTopkTokens tokens of item c (one token per wave at a time);
-// for E <= 256 all of a wave's token logits are loaded before the first selection
+// top-k + softmax for the kTopkTokens tokens of item c.  For E <= 256 a wave handles its 4
+// tokens together, with all of their logits loaded before the first selection.  The loads
+// are unconditional (clamped index, masked after): a load under a lane condition is waited
+// for inside its branch, which would serialise the loads.
 template <class SM>
 __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, SM &sm) {
   const int tid = otid(), wave = tid >> 6, lane = tid & 63, k = P.k, E = P.E;
   if (E <= 256) {
     constexpr int TPW = kTopkTokens / kWaves;  // tokens per wave
-    uint64_t key[TPW][4];
+    float v[TPW][4];
+    int t[TPW];
+    bool live[TPW];
+    int16_t *ids[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tt = wave + u * kWaves;
-      const float *Lr = P.logits + (size_t)(t0 + min(tt, ntok - 1)) * E;
+      live[u] = tt < ntok;
+      t[u] = t0 + min(tt, ntok - 1);
+      ids[u] = sm.u.r.ids + tt * k;
+      const float *Lr = P.logits + (size_t)t[u] * E;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = q * 64 + lane;
-        key[u][q] = e < E ? ((uint64_t)ordered_key(ld_coh(Lr + e)) << 32) | (uint32_t)(E - 1 - e) : 0ull;
-      }
+      for (int q = 0; q < 4; ++q) v[u][q] = ld_coh(Lr + min(q * 64 + lane, E - 1));
     }
+    asm volatile("" ::: "memory");  // all of the wave's loads are in flight before any is used
+    uint32_t key[TPW][4];
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int tt = wave + u * kWaves;
-      if (tt < ntok) topk_token<4>(P, t0 + tt, key[u], sm.u.r.ids + tt * k);
-    }
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) key[u][q] = (q * 64 + lane < E) ? ordered_key(v[u][q]) : 0u;
+    topk_group<4, TPW>(P, t, live, key, ids);
   } else {
     for (int tt = wave; tt < ntok; tt += kWaves) {
-      const float *Lr = P.logits + (size_t)(t0 + tt) * E;
-      uint64_t key[kMaxE / 64];
+      const int t[1] = {t0 + tt};
+      const bool live[1] = {true};
+      int16_t *const ids[1] = {sm.u.r.ids + tt * k};
+      const float *Lr = P.logits + (size_t)t[0] * E;
+      float v[kMaxE / 64];
 #pragma unroll
-      for (int q = 0; q < kMaxE / 64; ++q) {
-        const int e = q * 64 + lane;
-        key[q] = e < E ? ((uint64_t)ordered_key(ld_coh(Lr + e)) << 32) | (uint32_t)(E - 1 - e) : 0ull;
-      }
-      topk_token<kMaxE / 64>(P, t0 + tt, key, sm.u.r.ids + tt * k);
+      for (int q = 0; q < kMaxE / 64; ++q) v[q] = ld_coh(Lr + min(q * 64 + lane, E - 1));
+      uint32_t key[1][kMaxE / 64];
+#pragma unroll
+      for (int q = 0; q < kMaxE / 64; ++q) key[0][q] = (q * 64 + lane < E) ? ordered_key(v[q]) : 0u;
+      topk_group<kMaxE / 64, 1>(P, t, live, key, ids);
     }
   }
 }
@@ -790,12 +899,14 @@ template <class SM>
 __device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
   const int tid = otid(), k = P.k, E = P.E;
   const int t0 = c * kTopkTokens, ntok = min(kTopkTokens, P.T - t0);
+  if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
   if (P.phases & PH_IDS_GIVEN) {
-    for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = P.ids[(size_t)t0 * k + q];  // caller's input
+    for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = checked_id(P.ids[(size_t)t0 * k + q], E);  // caller's input
   } else {
     topk_tokens(P, t0, ntok, sm);
   }
   __syncthreads();
+  if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
   if (!(P.phases & PH_PERMUTE)) {
     wg_signal(P.ctrl + kSlotInts * C_KDONE);
     return;
@@ -836,7 +947,7 @@ template <class SM>
 __device__ __forceinline__ void scatter_item(const KParams &P, int c, SM &sm) {
   const int tid = otid(), k = P.k, E = P.E;
   const int t0 = c * P.tk, ntok = min(P.tk, P.T - t0);
-  for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = ld_coh(P.ids + (size_t)t0 * k + q);
+  for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = checked_id(ld_coh(P.ids + (size_t)t0 * k + q), E);
   __syncthreads();
   chunk_masks(P, ntok, sm);
   for (int e = tid; e < E; e += kThreads) {
@@ -866,7 +977,7 @@ __device__ __forceinline__ void store4(void *base, size_t idx, f4 v) {
 
 // gate/up item: rows (tokens) of one m-tile x gu_cols H columns; SwiGLU in registers
 template <int WT, int MG, class SM>
-__device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i, SM &sm) {
+__device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i, SM &sm, const Lds3 &lb) {
   using C = Core<WT, MG>;
   constexpr int NF = C::NF, NH = NF / 2;
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
@@ -916,7 +1027,7 @@ __device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i
   f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
-  C::template run<false>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, sm.u.act, P.d,
+  C::template run<false>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, lb, P.d,
                          ngroups);
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
 #pragma unroll
@@ -937,7 +1048,7 @@ __device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i
 
 // down item: rows of one m-tile x dn_cols output columns
 template <int WT, int MG, class SM>
-__device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm) {
+__device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm, const Lds3 &lb) {
   using C = Core<WT, MG>;
   constexpr int NF = C::NF;
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
@@ -979,7 +1090,7 @@ __device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm) {
   f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
-  C::template run<true>(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n * asz, sm.rows, sm.u.act, P.n,
+  C::template run<true>(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n * asz, sm.rows, lb, P.n,
                         ngroups);
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
 #pragma unroll
@@ -992,6 +1103,223 @@ __device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm) {
         if (c < P.d) store4<WT>(P.Y, (row0 + r) * (size_t)P.d + c, acc[a][b]);
       }
     }
+  }
+  wg_signal(P.ctrl + kSlotInts * C_DDONE);
+  return true;
+}
+
+// ---------------------------------------------------------------------------------
+// small m-tiles (at most 16 rows per expert, decode-sized problems): finer work units
+// streamed straight from HBM to registers, so the weight stream is spread evenly over
+// every workgroup and no unit waits for a long one.  A gate/up unit is 16 H columns
+// (wave w: the gate (w < 2) or up fragment over one half of K, the halves added in a
+// fixed order through LDS); a down unit is 64 output channels (wave w: 16 of them over
+// all of K).  Token rows past the tile's end repeat its last row (the same addresses, so
+// the loads coalesce) and are never stored.
+// ---------------------------------------------------------------------------------
+
+// acc[f] of NFR 16-row weight fragments against the same 16 token rows over nsteps
+// 64-byte weight steps.  w[f]: this lane's weight bytes (row j, k-group g) at the first
+// step; mk_a(): this lane's activation bytes for the same K positions (astep bytes per
+// step), evaluated after the first weight loads are issued, so that a lookup it depends on
+// (issued by the caller before) overlaps them.  D steps of loads stay in flight.  The loop
+// body has no branches: steps past the end load one fixed line and multiply a zeroed
+// activation, so every step issues the same memory operations; the first D steps are
+// peeled so that the loads pending at the loop head are always in the same (interleaved)
+// order, and the compiler can wait for exactly the step it consumes.  fp8: every two
+// steps (128 K) close a scale block, whose partial sum is scaled by sc[f][block] before
+// joining the result.
+template <int WT, bool ACOH, int NFR, class MkA>
+__device__ __forceinline__ void stream_frags(f4 (&acc)[NFR], const char *const (&w)[NFR], MkA mk_a, int astep,
+                                             int nsteps, const float *const (&sc)[NFR]) {
+  constexpr int D = 8;
+  constexpr int NA = WT == WFP8 ? 2 : 1;  // 16-byte activation loads per step
+  const char *wdummy = reinterpret_cast<const char *>(uni64(reinterpret_cast<uint64_t>(w[0])));
+  // fp8 block scales: lane l holds the scales of blocks l and l + 64 (read back with
+  // readlane), so the loop issues no memory operation besides the stream itself
+  const int nblk = nsteps >> 1;
+  float scl0[NFR], scl1[NFR];
+#pragma unroll
+  for (int f = 0; f < NFR; ++f) {
+    scl0[f] = scl1[f] = 0.f;
+    if constexpr (WT == WFP8) {
+      const int lane = otid() & 63;
+      scl0[f] = sc[f][min(lane, nblk - 1)];
+      scl1[f] = sc[f][min(lane + 64, nblk - 1)];
+    }
+  }
+  uint4 wq[D][NFR], aq[D][NA];
+  auto load_w = [&](int slot, int t) {
+#pragma unroll
+    for (int f = 0; f < NFR; ++f) wq[slot][f] = ld_stream16(t < nsteps ? w[f] + (size_t)t * 64 : wdummy);
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    load_w(u, u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const char *a = mk_a();
+  const char *adummy = reinterpret_cast<const char *>(uni64(reinterpret_cast<uint64_t>(a)));
+  auto load_a = [&](int slot, int t) {
+#pragma unroll
+    for (int x = 0; x < NA; ++x) {
+      const char *ap = t < nsteps ? a + (size_t)t * astep + x * 16 : adummy;
+      if constexpr (ACOH) aq[slot][x] = ld_coh16(ap);
+      else aq[slot][x] = ld_glob16(ap);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    load_a(u, u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  f4 blk[NFR];
+#pragma unroll
+  for (int f = 0; f < NFR; ++f) acc[f] = blk[f] = f4{0.f, 0.f, 0.f, 0.f};
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+  auto step = [&](int t, int u) {
+    const bool real = t + u < nsteps;
+    const uint4 a0 = real ? aq[u][0] : z4, a1 = real ? aq[u][NA - 1] : z4;
+#pragma unroll
+    for (int f = 0; f < NFR; ++f) {
+      if constexpr (WT == WFP8) {
+        blk[f] = mfma_step<WT>(wq[u][f], a0, a1, blk[f]);
+        if (u & 1) {
+          const int b = min((t + u) >> 1, nblk - 1);
+          const float scb =
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b < 64 ? scl0[f] : scl1[f]), b & 63));
+          acc[f] += blk[f] * scb;
+          blk[f] = f4{0.f, 0.f, 0.f, 0.f};
+        }
+      } else {
+        acc[f] = mfma_step<WT>(wq[u][f], a0, a0, acc[f]);
+      }
+    }
+    // refill the slot right behind the step it served (D steps in flight at all times)
+    load_w(u, t + u + D);
+    load_a(u, t + u + D);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u) step(0, u);  // peeled first block
+  for (int t = D; t < nsteps; t += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) step(t, u);
+  }
+}
+
+// byte offset of lane k-group g's activation elements within one weight step
+template <int WT> __device__ __forceinline__ int act_lane_off(int g) {
+  if constexpr (WT == WFP8) return g * 32;  // 16 fp8 weights -> 16 bf16 activations (2 x 16 B)
+  else return g * 16;                       // 16 bytes of the same element width
+}
+
+template <int WT, class SM>
+__device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i, SM &sm) {
+  constexpr int WSZ = Ty<WT>::WSZ, ASZ = Ty<WT>::ASZ, KU = Ty<WT>::KU;
+  const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
+  const int gm = i / P.nt_gu, s = i % P.nt_gu;
+  int e, row0, m, counter;
+  size_t hrow0;
+  if (shared) {
+    e = P.E;
+    row0 = gm * 16;
+    m = min(16, P.T - row0);
+    hrow0 = (size_t)P.T * P.k + row0;
+    counter = gm;
+  } else {
+    const int4 ds = ld_coh_int4(P.desc + gm);
+    e = uni(ds.x);
+    row0 = uni(ds.y);
+    m = uni(ds.z);
+    hrow0 = row0;
+    counter = P.n_shmt + gm;
+  }
+  const int rr = min(j, m - 1);
+  // the permutation lookup is issued before the weight stream starts and consumed after
+  // its first loads (stream_frag's mk_a), so the two latencies overlap
+  const int slot = shared ? 0 : ld_coh(P.perm + row0 + rr);
+  __builtin_amdgcn_sched_barrier(0);
+  // wave 0/1: gate rows, wave 2/3: up rows; K half wv & 1
+  const int kh = P.d / 2, k0 = (wv & 1) * kh;
+  const char *wb = reinterpret_cast<const char *>(wv < 2 ? (shared ? P.shg : P.wg) : (shared ? P.shu : P.wu));
+  const size_t emat = shared ? 0 : (size_t)e * P.n * P.d * WSZ;
+  const char *w = wb + emat + (size_t)(16 * s + j) * P.d * WSZ + (size_t)k0 * WSZ + g * 16;
+  auto mk_a = [&]() {
+    const int tok = min(max(shared ? row0 + rr : slot / P.k, 0), P.T - 1);
+    return reinterpret_cast<const char *>(P.x) + ((size_t)tok * P.d + k0) * ASZ + act_lane_off<WT>(g);
+  };
+  const float *sc[1] = {nullptr};
+  if constexpr (WT == WFP8) {
+    const int nkb = P.d / 128;
+    sc[0] = (wv < 2 ? (shared ? P.shsg : P.sg) : (shared ? P.shsu : P.su)) +
+            (shared ? 0 : (size_t)e * (P.n / 128) * nkb) + (size_t)((16 * s) / 128) * nkb + k0 / 128;
+  }
+  if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
+  const char *wf[1] = {w};
+  f4 pa[1];
+  stream_frags<WT, false, 1>(pa, wf, mk_a, KU * ASZ, kh / KU, sc);
+  const f4 part = pa[0];
+  if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
+  sm.u.red[wv][lane] = part;
+  __syncthreads();
+  if (wv == 0 && j < m) {
+    const f4 gs = sm.u.red[0][lane] + sm.u.red[1][lane];
+    const f4 us = sm.u.red[2][lane] + sm.u.red[3][lane];
+    f4 h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) h[q] = silu_mul(gs[q], us[q]);
+    store4<WT>(P.H, (hrow0 + j) * (size_t)P.n + 16 * s + 4 * g, h);
+  }
+  wg_signal(P.gudone + counter);
+}
+
+template <int WT, class SM>
+__device__ __forceinline__ bool down_unit(const KParams &P, int i, SM &sm) {
+  constexpr int WSZ = Ty<WT>::WSZ, ASZ = Ty<WT>::ASZ, KU = Ty<WT>::KU;
+  const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
+  const int gm = i / P.nt_dn, ob = i % P.nt_dn;
+  if (!wg_wait(P.gudone + gm, P.nt_gu, P.ctrl + kSlotInts * C_ERR, sm)) return false;
+  const bool shared = gm < P.n_shmt;
+  int e, m;
+  size_t hrow0;
+  if (shared) {
+    e = P.E;
+    const int t0 = gm * 16;
+    m = min(16, P.T - t0);
+    hrow0 = (size_t)P.T * P.k + t0;
+  } else {
+    const int4 ds = ld_coh_int4(P.desc + gm - P.n_shmt);
+    e = uni(ds.x);
+    hrow0 = (size_t)uni(ds.y);
+    m = uni(ds.z);
+  }
+  constexpr int NFR = 1;
+  const int o0 = ob * (64 * NFR) + wv * 16 * NFR;  // this wave's 16 * NFR output channels
+  const char *wb = reinterpret_cast<const char *>(shared ? P.shd : P.wd) + (shared ? 0 : (size_t)e * P.d * P.n * WSZ);
+  const char *w[NFR];
+#pragma unroll
+  for (int f = 0; f < NFR; ++f) w[f] = wb + (size_t)(o0 + 16 * f + j) * P.n * WSZ + g * 16;
+  auto mk_a = [&]() {
+    return reinterpret_cast<const char *>(P.H) + (hrow0 + min(j, m - 1)) * (size_t)P.n * ASZ + act_lane_off<WT>(g);
+  };
+  const float *sc[NFR];
+#pragma unroll
+  for (int f = 0; f < NFR; ++f) {
+    sc[f] = nullptr;
+    if constexpr (WT == WFP8) {
+      const int nkb = P.n / 128;
+      sc[f] = (shared ? P.shsd : P.sd) + (shared ? 0 : (size_t)e * (P.d / 128) * nkb) +
+              (size_t)((o0 + 16 * f) / 128) * nkb;
+    }
+  }
+  if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
+  f4 acc[NFR];
+  stream_frags<WT, true, NFR>(acc, w, mk_a, KU * ASZ, P.n / KU, sc);
+  if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
+  if (j < m) {
+#pragma unroll
+    for (int f = 0; f < NFR; ++f) store4<WT>(P.Y, (hrow0 + j) * (size_t)P.d + o0 + 16 * f + 4 * g, acc[f]);
   }
   wg_signal(P.ctrl + kSlotInts * C_DDONE);
   return true;
@@ -1064,6 +1392,10 @@ template <int WT, int MG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occ<WT, MG>::waves)))
 void moe_persistent(KParams P) {
   __shared__ Smem<WT, MG> sm;
+  __shared__ __attribute__((aligned(16))) char act0[ActBuf<WT, MG>::BYTES];
+  __shared__ __attribute__((aligned(16))) char act1[ActBuf<WT, MG>::BYTES];
+  __shared__ __attribute__((aligned(16))) char act2[ActBuf<WT, MG>::BYTES];
+  const Lds3 lb{act0, act1, act2};
   const int tid = threadIdx.x;
   int *ctrl = P.ctrl;
   int *err = ctrl + kSlotInts * C_ERR;
@@ -1099,7 +1431,7 @@ void moe_persistent(KParams P) {
       kind = K_ZERO;
     } else if ((i -= n_Z) < n_L) {
       if constexpr (MG == 1) logits_item_split<WT>(P, i, sm);
-      else logits_item_tile<WT, MG>(P, i, sm);
+      else logits_item_tile<WT, MG>(P, i, sm, lb);
       wg_signal(ctrl + kSlotInts * C_LDONE);
       kind = K_ROUTER;
     } else if ((i -= n_L) < n_K) {
@@ -1118,7 +1450,8 @@ void moe_persistent(KParams P) {
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
       }
-      gateup_item<WT, MG>(P, true, i, sm);
+      if constexpr (MG == 1) gateup_unit<WT>(P, true, i, sm);
+      else gateup_item<WT, MG>(P, true, i, sm, lb);
       kind = K_SHGU;
     } else if ((i -= n_SG) < n_S) {
       if (!plan_seen) {
@@ -1147,14 +1480,19 @@ void moe_persistent(KParams P) {
           if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
           zero_seen = true;
         }
-        gateup_item<WT, MG>(P, false, i, sm);
+        if constexpr (MG == 1) gateup_unit<WT>(P, false, i, sm);
+        else gateup_item<WT, MG>(P, false, i, sm, lb);
         kind = K_GU;
       } else if ((i -= n_G) < n_D) {
         if (!zero_seen) {  // the dependency counters must be cleared before they are read
           if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
           zero_seen = true;
         }
-        if (!down_item<WT, MG>(P, i, sm)) break;
+        if constexpr (MG == 1) {
+          if (!down_unit<WT>(P, i, sm)) break;
+        } else {
+          if (!down_item<WT, MG>(P, i, sm, lb)) break;
+        }
         kind = K_DN;
       } else if ((i -= n_D) < P.n_comb) {
         if (!dn_seen) {

@@ -12,6 +12,9 @@
 #include "moe.h"
 
 namespace moe {
+// internal linkage: every translation unit that includes this header gets its own copy, so
+// two objects built with different settings can never exchange definitions at link time
+namespace {
 
 constexpr int kThreads = 256;          // threads per workgroup (4 wave64)
 constexpr int kWaves = 4;
@@ -40,11 +43,11 @@ struct Tiles {
   int mg;          // 16-row token groups per m-tile (1, 2, 4 or 8)
   int bm;          // rows per m-tile = 16 * mg
   int nf;          // 16-row weight fragments per wave (2 when mg == 1, else 4)
-  int gu_cols;     // H columns per gate/up item: 4 waves x nf/2 x 16
-  int dn_cols;     // output columns per down item: 4 waves x nf x 16
+  int gu_cols;     // H columns per gate/up item: 4 waves x nf/2 x 16 (16 when mg == 1)
+  int dn_cols;     // output columns per down item: 4 waves x nf x 16 (64 when mg == 1)
   int tk;          // tokens per scatter chunk (tk <= 128, tk * k <= 1024)
   int rt_tokens;   // router item: tokens x experts (16 x 16 split over the 4 waves when
-  int rt_experts;  //   mg == 1, else min(bm, 64) x 64*nf on the expert tile core)
+  int rt_experts;  //   mg == 1, else 16 x 128 on the 16-row expert tile core)
 };
 
 struct Layout {
@@ -97,13 +100,15 @@ inline Tiles choose_tiles(const moe_problem *p) {
   t.mg = mean_rows <= 16 ? 1 : mean_rows <= 32 ? 2 : mean_rows <= 64 ? 4 : 8;
   t.bm = 16 * t.mg;
   t.nf = t.mg == 1 ? 2 : 4;
-  t.gu_cols = 4 * (t.nf / 2) * 16;
-  t.dn_cols = 4 * t.nf * 16;
+  // mg == 1: small units streamed by single waves (gate/up: 16 columns, the waves split
+  // gate/up and the two halves of K; down: 16 channels per wave)
+  t.gu_cols = t.mg == 1 ? 16 : 4 * (t.nf / 2) * 16;
+  t.dn_cols = t.mg == 1 ? 64 : 4 * t.nf * 16;
   t.tk = kMaxChunkSlots / p->k;
   if (t.tk > kMaxChunkTokens) t.tk = kMaxChunkTokens;
   if (t.tk < 1) t.tk = 1;
-  t.rt_tokens = 16 * (t.mg > 4 ? 4 : t.mg);
-  t.rt_experts = t.mg == 1 ? 16 : 64 * t.nf;
+  t.rt_tokens = 16;
+  t.rt_experts = t.mg == 1 ? 16 : 128;
   return t;
 }
 
@@ -174,4 +179,5 @@ inline PhaseCounts phase_counts(const Layout &L, int phases) {
   return c;
 }
 
+}  // namespace
 }  // namespace moe

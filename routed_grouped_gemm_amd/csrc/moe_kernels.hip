@@ -654,24 +654,27 @@ __device__ __forceinline__ void wave_excl_scan(const int *in, int *out, int N, i
   if (lane == 63) out[N] = incl;
 }
 
-// wave-wide max (MAX) or min of a 32-bit value, returned in every lane: row-shift and
-// row-broadcast DPP steps (VALU data movement, no LDS round trips), result read from lane 63
-template <bool MAX>
-__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
-#define MOE_DPP_RED(CTRL, ROWM, BANKM)                                              \
-  {                                                                                \
-    const uint32_t o = __builtin_amdgcn_update_dpp(v, v, CTRL, ROWM, BANKM, false); \
-    v = MAX ? (o > v ? o : v) : (o < v ? o : v);                                   \
+// wave-wide unsigned max of N independent 32-bit values (each returned in every lane):
+// row-shift and row-broadcast DPP steps (VALU data movement, no LDS round trips), the N
+// reductions interleaved step by step so that their latencies overlap; out-of-row lanes
+// read 0 (the identity of unsigned max), which lets each step be a single DPP max
+template <int N>
+__device__ __forceinline__ void wave_max_u32(uint32_t (&v)[N]) {
+#define MOE_DPP_MAX(CTRL, ROWM, BANKM)                                                      \
+  _Pragma("unroll") for (int i = 0; i < N; ++i) {                                          \
+    const uint32_t o = __builtin_amdgcn_update_dpp(0u, v[i], CTRL, ROWM, BANKM, true);    \
+    v[i] = o > v[i] ? o : v[i];                                                            \
   }
-  MOE_DPP_RED(0x111, 0xf, 0xf)  // row_shr:1
-  MOE_DPP_RED(0x112, 0xf, 0xf)  // row_shr:2
-  MOE_DPP_RED(0x113, 0xf, 0xf)  // row_shr:3
-  MOE_DPP_RED(0x114, 0xf, 0xe)  // row_shr:4
-  MOE_DPP_RED(0x118, 0xf, 0xc)  // row_shr:8
-  MOE_DPP_RED(0x142, 0xa, 0xf)  // row_bcast:15
-  MOE_DPP_RED(0x143, 0xc, 0xf)  // row_bcast:31
-#undef MOE_DPP_RED
-  return __builtin_amdgcn_readlane(v, 63);
+  MOE_DPP_MAX(0x111, 0xf, 0xf)  // row_shr:1
+  MOE_DPP_MAX(0x112, 0xf, 0xf)  // row_shr:2
+  MOE_DPP_MAX(0x113, 0xf, 0xf)  // row_shr:3
+  MOE_DPP_MAX(0x114, 0xf, 0xe)  // row_shr:4
+  MOE_DPP_MAX(0x118, 0xf, 0xc)  // row_shr:8
+  MOE_DPP_MAX(0x142, 0xa, 0xf)  // row_bcast:15
+  MOE_DPP_MAX(0x143, 0xc, 0xf)  // row_bcast:31
+#undef MOE_DPP_MAX
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = __builtin_amdgcn_readlane(v[i], 63);
 }
 
 // The plan: counts -> offsets (exclusive scan), m-tile counts -> m-tile offsets, the
@@ -796,16 +799,21 @@ __device__ __forceinline__ void topk_group(const KParams &P, const int (&t)[TPW]
       uint32_t b = key[u][0];
 #pragma unroll
       for (int q = 1; q < NQ; ++q) b = key[u][q] > b ? key[u][q] : b;
-      m[u] = wave_reduce_u32<true>(b);
+      m[u] = b;
     }
+    wave_max_u32<TPW>(m);
+    // the lowest id holding the maximum: the max of the complemented ids (0 = no match)
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      uint32_t x = 0xffffffffu;
+      uint32_t x = 0u;
 #pragma unroll
       for (int q = NQ - 1; q >= 0; --q)
-        if (key[u][q] == m[u]) x = (uint32_t)(q * 64 + lane);  // the lowest matching id of this lane
-      c[u] = wave_reduce_u32<false>(x);
+        if (key[u][q] == m[u]) x = ~(uint32_t)(q * 64 + lane);  // this lane's lowest matching id
+      c[u] = x;
     }
+    wave_max_u32<TPW>(c);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) c[u] = ~c[u];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
 #pragma unroll

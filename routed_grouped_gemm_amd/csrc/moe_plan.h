@@ -97,7 +97,9 @@ inline moe_status validate_problem(const moe_problem *p) {
 inline Tiles choose_tiles(const moe_problem *p) {
   Tiles t;
   const double mean_rows = p->E > 0 ? double(p->T) * p->k / p->E : 0.0;
-  t.mg = mean_rows <= 16 ? 1 : mean_rows <= 32 ? 2 : mean_rows <= 64 ? 4 : 8;
+  // the row count of an expert spreads around the mean by about its square root: pick the
+  // tile so that most experts fit in one m-tile (each extra m-tile re-reads the weights)
+  t.mg = mean_rows <= 8 ? 1 : mean_rows <= 20 ? 2 : mean_rows <= 44 ? 4 : 8;
   t.bm = 16 * t.mg;
   t.nf = t.mg == 1 ? 2 : 4;
   // mg == 1: small units streamed by single waves (gate/up: 16 columns, the waves split

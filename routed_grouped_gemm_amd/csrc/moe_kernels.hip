@@ -1137,10 +1137,9 @@ __device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm, const
 // order, and the compiler can wait for exactly the step it consumes.  fp8: every two
 // steps (128 K) close a scale block, whose partial sum is scaled by sc[f][block] before
 // joining the result.
-template <int WT, bool ACOH, int NFR, class MkA>
+template <int WT, bool ACOH, int NFR, int D, class MkA>
 __device__ __forceinline__ void stream_frags(f4 (&acc)[NFR], const char *const (&w)[NFR], MkA mk_a, int astep,
                                              int nsteps, const float *const (&sc)[NFR]) {
-  constexpr int D = 8;
   constexpr int NA = WT == WFP8 ? 2 : 1;  // 16-byte activation loads per step
   const char *wdummy = reinterpret_cast<const char *>(uni64(reinterpret_cast<uint64_t>(w[0])));
   // fp8 block scales: lane l holds the scales of blocks l and l + 64 (read back with
@@ -1223,7 +1222,7 @@ template <int WT> __device__ __forceinline__ int act_lane_off(int g) {
 }
 
 template <int WT, class SM>
-__device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i, SM &sm) {
+__device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i, SM &sm, bool deep) {
   constexpr int WSZ = Ty<WT>::WSZ, ASZ = Ty<WT>::ASZ, KU = Ty<WT>::KU;
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int gm = i / P.nt_gu, s = i % P.nt_gu;
@@ -1266,7 +1265,8 @@ __device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
   const char *wf[1] = {w};
   f4 pa[1];
-  stream_frags<WT, false, 1>(pa, wf, mk_a, KU * ASZ, kh / KU, sc);
+  if (deep) stream_frags<WT, false, 1, 8>(pa, wf, mk_a, KU * ASZ, kh / KU, sc);
+  else stream_frags<WT, false, 1, 4>(pa, wf, mk_a, KU * ASZ, kh / KU, sc);
   const f4 part = pa[0];
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
   sm.u.red[wv][lane] = part;
@@ -1283,7 +1283,7 @@ __device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i
 }
 
 template <int WT, class SM>
-__device__ __forceinline__ bool down_unit(const KParams &P, int i, SM &sm) {
+__device__ __forceinline__ bool down_unit(const KParams &P, int i, SM &sm, bool deep) {
   constexpr int WSZ = Ty<WT>::WSZ, ASZ = Ty<WT>::ASZ, KU = Ty<WT>::KU;
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int gm = i / P.nt_dn, ob = i % P.nt_dn;
@@ -1323,7 +1323,8 @@ __device__ __forceinline__ bool down_unit(const KParams &P, int i, SM &sm) {
   }
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
   f4 acc[NFR];
-  stream_frags<WT, true, NFR>(acc, w, mk_a, KU * ASZ, P.n / KU, sc);
+  if (deep) stream_frags<WT, true, NFR, 8>(acc, w, mk_a, KU * ASZ, P.n / KU, sc);
+  else stream_frags<WT, true, NFR, 4>(acc, w, mk_a, KU * ASZ, P.n / KU, sc);
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
   if (j < m) {
 #pragma unroll
@@ -1458,7 +1459,7 @@ void moe_persistent(KParams P) {
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
       }
-      if constexpr (MG == 1) gateup_unit<WT>(P, true, i, sm);
+      if constexpr (MG == 1) gateup_unit<WT>(P, true, i, sm, 2 * n_SG <= kWaves * (int)gridDim.x);
       else gateup_item<WT, MG>(P, true, i, sm, lb);
       kind = K_SHGU;
     } else if ((i -= n_SG) < n_S) {
@@ -1479,6 +1480,10 @@ void moe_persistent(KParams P) {
       if (n_mt < 0) n_mt = uni(ld_relaxed(ctrl + kSlotInts * C_NMT));
       const int n_G = n_mt * P.nt_gu;
       const int n_D = (n_mt + P.n_shmt) * P.nt_dn;
+      // small-tile units: a deep prefetch (8 steps) when the units are too few to keep the
+      // memory system busy, else a shallow one (4 steps): with every wave of the grid
+      // streaming, more requests in flight only add contention
+      const bool deep = 2 * n_G <= kWaves * (int)gridDim.x;
       if (i < n_G) {
         if (!scat_seen) {
           if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S, err, sm)) break;
@@ -1488,7 +1493,7 @@ void moe_persistent(KParams P) {
           if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
           zero_seen = true;
         }
-        if constexpr (MG == 1) gateup_unit<WT>(P, false, i, sm);
+        if constexpr (MG == 1) gateup_unit<WT>(P, false, i, sm, deep);
         else gateup_item<WT, MG>(P, false, i, sm, lb);
         kind = K_GU;
       } else if ((i -= n_G) < n_D) {
@@ -1497,7 +1502,7 @@ void moe_persistent(KParams P) {
           zero_seen = true;
         }
         if constexpr (MG == 1) {
-          if (!down_unit<WT>(P, i, sm)) break;
+          if (!down_unit<WT>(P, i, sm, deep)) break;
         } else {
           if (!down_item<WT, MG>(P, i, sm, lb)) break;
         }

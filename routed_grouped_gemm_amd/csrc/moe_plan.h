@@ -28,6 +28,7 @@ constexpr int kMaxChunkSlots = 1024;   // (token, slot) pairs per chunk
 constexpr int kCombineTokens = 1;      // combine item: 1 token
 constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroing item
 
+
 // control-block slots (one int32 each, at int index slot * kSlotInts): a poll of one
 // counter never shares a cache line or channel with the ticket counter or another counter
 enum CtrlSlot : int {

@@ -46,6 +46,18 @@
  *   sh_s_gate, sh_s_up [n/128, d/128], sh_s_down [d/128, n/128]; it has weight 1 and
  *   runs on every token (GC-MoE article, "two MMA implementations": fused shared experts).
  *
+ * Expert weight layout (moe_problem.w_layout).  MOE_W_ROWMAJOR: the [rows, K] matrices above
+ * as they are; the compute calls do not take them (MOE_ERR_UNSUPPORTED), moe_pack_weights
+ * converts them.  MOE_W_PACKED, the layout moe_forward and moe_forward_ex read: each matrix
+ * is cut into fragments of 16 consecutive rows, and a
+ * fragment is stored K step by K step, a step being 64 bytes of each of its 16 rows (32 bf16,
+ * 64 fp8 or 16 fp32 values) laid out as one contiguous 1 KB block in which row r's bytes
+ * [16 g, 16 g + 16) of the step sit at offset 16 * (16 g + r).  This is the register layout of
+ * the 16-row operand of the MFMA instructions, so every weight load of the kernel reads 1 KB
+ * of contiguous memory; moe_pack_weights converts row-major weights once, at load time.  The
+ * packed matrices have the same size and the same per-expert offsets; scales and the router
+ * are never packed.
+ *
  * Supported (act dtype, weight dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
  * Shape limits: 1 <= k <= E <= 1024, d and n multiples of 256, T*k < 2^31.
  */
@@ -61,7 +73,7 @@ extern "C" {
 
 typedef struct ihipStream_t *hipStream_t;
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -75,6 +87,8 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 /* OCP e4m3fn */ } moe_dtype;
 
+typedef enum { MOE_W_ROWMAJOR = 0, MOE_W_PACKED = 1 } moe_weight_layout;
+
 /* (host) problem descriptor; dtype fields hold moe_dtype values. */
 typedef struct {
   int64_t T;          /* tokens in this call (the M of the grouped GEMM), T >= 0         */
@@ -86,6 +100,7 @@ typedef struct {
   int32_t act_dtype;  /* MOE_F32 or MOE_BF16: hidden, w_router, out                       */
   int32_t w_dtype;    /* MOE_F32, MOE_BF16 or MOE_FP8_E4M3: expert weights               */
   int32_t scale_block;/* 128 when w_dtype == MOE_FP8_E4M3, else 0                         */
+  int32_t w_layout;   /* moe_weight_layout of w_gate, w_up, w_down and the shared expert     */
 } moe_problem;
 
 /* (host) struct of device pointers to the expert weights (layouts above). */
@@ -164,6 +179,14 @@ moe_status moe_forward_ex(const moe_problem *p, const void *hidden, const void *
                           const float *bias, const moe_weights *w, void *out,
                           const moe_route_out *route_out, void *ws, size_t ws_bytes,
                           hipStream_t stream, const moe_launch_options *opts);
+
+/* Converts row-major expert weights to the packed layout (see above), on `stream`: every
+ * matrix of src (w_gate, w_up, w_down and, when p->n_shared, sh_gate, sh_up, sh_down) is
+ * written, permuted, to the matching pointer of dst, which must not overlap it.  Scale
+ * pointers are not used (scales keep their layout).  p->w_layout is ignored.  No workspace,
+ * no allocation; validation as for the compute calls. */
+moe_status moe_pack_weights(const moe_problem *p, const moe_weights *src, const moe_weights *dst,
+                            hipStream_t stream);
 
 /* Synchronizes `stream`, then reports MOE_ERR_DEVICE_FAULT if a device-side wait of an
  * earlier call on this workspace timed out (or the workspace was never initialised),

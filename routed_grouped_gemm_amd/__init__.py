@@ -5,9 +5,10 @@ kernels.  torch is used for device memory (tensor storage and data_ptr()) and fo
 the current HIP stream; nothing here computes any part of the layer.
 
     import routed_grouped_gemm_amd as moe
-    p = moe.problem(T, d, n, E, k, act="bf16", w="bf16")
+    p = moe.problem(T, d, n, E, k, act="bf16", w="bf16", layout="packed")
+    packed = moe.pack_weights(p, weights)         # once, at load time (rowmajor: skip)
     ws = moe.alloc_workspace(p)                   # caller-owned, initialised once
-    out = moe.forward(p, hidden, w_router, None, weights, ws)
+    out = moe.forward(p, hidden, w_router, None, packed, ws)
 
 If the library has not been built, importing works but every call raises; there
 is no fallback path.
@@ -21,8 +22,9 @@ import re
 import torch
 
 __all__ = ["MoEError", "problem", "workspace_size", "alloc_workspace", "workspace_init", "route",
-           "permute", "forward", "last_device_error", "abi_version", "status_string", "MoELayer",
-           "LIB_PATH", "HEADER_PATH", "header_functions", "F32", "BF16", "FP8_E4M3"]
+           "permute", "forward", "pack_weights", "last_device_error", "abi_version", "status_string",
+           "MoELayer", "LIB_PATH", "HEADER_PATH", "header_functions", "F32", "BF16", "FP8_E4M3",
+           "ROWMAJOR", "PACKED"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
@@ -30,6 +32,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe.h")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 _DT = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+ROWMAJOR, PACKED = 0, 1
+_LAYOUT = {"rowmajor": ROWMAJOR, "packed": PACKED}
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
            3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP", 5: "MOE_ERR_DEVICE_FAULT"}
 
@@ -43,7 +47,7 @@ class MoEError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("n", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("w_dtype", ctypes.c_int32), ("scale_block", ctypes.c_int32)]
+                ("w_dtype", ctypes.c_int32), ("scale_block", ctypes.c_int32), ("w_layout", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -81,12 +85,13 @@ def _load():
     L.moe_permute.argtypes = [P, VP, VP, VP, VP, VP, VP, SZ, VP]
     L.moe_forward.argtypes = [P, VP, VP, VP, ctypes.POINTER(Weights), VP, ctypes.POINTER(RouteOut), VP, SZ, VP]
     L.moe_forward_ex.argtypes = L.moe_forward.argtypes + [ctypes.POINTER(LaunchOptions)]
+    L.moe_pack_weights.argtypes = [P, ctypes.POINTER(Weights), ctypes.POINTER(Weights), VP]
     L.moe_last_device_error.argtypes = [VP, VP]
     L.moe_status_string.argtypes = [I]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_abi_version.argtypes = []
     for fn in ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_permute", "moe_forward",
-               "moe_forward_ex", "moe_last_device_error", "moe_abi_version"):
+               "moe_forward_ex", "moe_pack_weights", "moe_last_device_error", "moe_abi_version"):
         getattr(L, fn).restype = I
     _lib = L
     return L
@@ -130,10 +135,10 @@ def status_string(code: int) -> str:
     return _load().moe_status_string(code).decode()
 
 
-def problem(T, d, n, E, k, n_shared=0, act="bf16", w="bf16") -> Problem:
+def problem(T, d, n, E, k, n_shared=0, act="bf16", w="bf16", layout="rowmajor") -> Problem:
     wd = _DT[w]
     return Problem(int(T), int(d), int(n), int(E), int(k), int(n_shared), _DT[act], wd,
-                   128 if wd == FP8_E4M3 else 0)
+                   128 if wd == FP8_E4M3 else 0, _LAYOUT[layout])
 
 
 def workspace_size(p: Problem) -> int:
@@ -229,6 +234,21 @@ def forward(p: Problem, hidden, w_router, bias, weights, ws, out=None, route_out
     return (out, rdict) if route_out else out
 
 
+_MATS = ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")
+
+
+def pack_weights(p: Problem, weights: dict) -> dict:
+    """Row-major expert weights -> a new dict whose matrices are in the packed layout
+    (moe_pack_weights, on the current stream); scales are passed through unchanged."""
+    out = dict(weights)
+    for key in _MATS:
+        if weights.get(key) is not None:
+            out[key] = torch.empty_like(weights[key])
+    _check(_load().moe_pack_weights(ctypes.byref(p), ctypes.byref(make_weights(weights)),
+                                    ctypes.byref(make_weights(out)), _stream()), "moe_pack_weights")
+    return out
+
+
 def last_device_error(ws) -> int:
     """Synchronizes the current stream; 0 if no device-side fault was flagged."""
     return _load().moe_last_device_error(_ptr(ws), _stream())
@@ -238,15 +258,17 @@ class MoELayer:
     """Holds device weights and a workspace; call with hidden [T, d] for the layer output."""
 
     def __init__(self, d, n, E, k, w_router, weights: dict, bias=None, n_shared=0, act="bf16", w="bf16"):
+        """weights: row-major expert weights; they are packed once, here."""
         self.d, self.n, self.E, self.k, self.n_shared, self.act, self.w = d, n, E, k, n_shared, act, w
-        self.w_router, self.bias, self.weights = w_router, bias, weights
-        self._W = make_weights(weights)
+        self.w_router, self.bias = w_router, bias
+        self.weights = pack_weights(problem(1, d, n, E, k, n_shared, act, w), weights)
+        self._W = make_weights(self.weights)
         self._ws = None
         self._ws_T = -1
 
     def __call__(self, hidden, route_out=False):
         T = hidden.shape[0]
-        p = problem(T, self.d, self.n, self.E, self.k, self.n_shared, self.act, self.w)
+        p = problem(T, self.d, self.n, self.E, self.k, self.n_shared, self.act, self.w, layout="packed")
         if self._ws is None or workspace_size(p) > self._ws.numel():
             self._ws = alloc_workspace(p, hidden.device)
         return forward(p, hidden, self.w_router, self.bias, self._W, self._ws, route_out=route_out)

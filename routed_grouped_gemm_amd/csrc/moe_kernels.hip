@@ -101,6 +101,9 @@ struct KParams {
   long long trace_cap;
 };
 
+// work item kinds (trace records)
+enum ItemKind : int { K_ZERO = 0, K_ROUTER = 1, K_TOPK = 2, K_SHGU = 3, K_SCATTER = 4, K_GU = 5, K_DN = 6, K_COMB = 7 };
+
 // ---------------------------------------------------------------------------------
 // small helpers
 // ---------------------------------------------------------------------------------
@@ -118,6 +121,15 @@ __device__ __forceinline__ uint64_t uni64(uint64_t v) {
 __device__ __forceinline__ const char *laundered(const char *p) {
   asm volatile("" : "+v"(p));
   return p;
+}
+
+// Expert weights are in the packed fragment layout: the 16 rows of a fragment are stored K
+// step by K step, each step (64 bytes of each row) one contiguous 1 KB block in MFMA lane
+// order, so lane l's 16 bytes of step s sit at fragment + s * kWStep + 16 * l.  A fragment
+// spans the same bytes as its 16 rows in row-major order (it starts at row r0's offset).
+constexpr int kWStep = 1024;
+__device__ __forceinline__ const char *frag_ptr(const void *mat, int r0, size_t rb, int lane) {
+  return reinterpret_cast<const char *>(mat) + (size_t)r0 * rb + lane * 16;
 }
 
 __device__ __forceinline__ int otid() {
@@ -380,7 +392,9 @@ template <int WT, int MG> struct Core {
 
   // COH: the activation rows were written earlier in this launch (H), so they are read
   // with the device-coherent policy
-  template <bool COH>
+  // WSTEP: bytes between consecutive 64-byte K steps of a weight fragment (kWStep for the
+  // packed expert weights, 64 for the row-major router rows)
+  template <bool COH, int WSTEP>
   __device__ static void run(f4 (&acc)[NF][MG], const char *const (&wrow)[NF], const float *const (&sc)[NF],
                              const char *abase, size_t arow_bytes, const int *rows, const Lds3 &lb, int K,
                              int ngroups) {
@@ -427,7 +441,7 @@ template <int WT, int MG> struct Core {
       for (int f = 0; f < FL; ++f)
 #pragma unroll
         for (int a = 0; a < NF; ++a)
-          W[a][f] = ld_stream16(real ? wr[a] + (size_t)c * (FL * 64) + f * 64 : wdummy);
+          W[a][f] = ld_stream16(real ? wr[a] + (size_t)c * (FL * WSTEP) + f * WSTEP : wdummy);
     };
     // small tiles compute every token group (rows past the tile's end repeat its last
     // row, valid data whose results are not stored); large tiles skip absent groups,
@@ -618,8 +632,8 @@ __device__ __forceinline__ void logits_item_tile(const KParams &P, int i, SM &sm
     sc[a] = nullptr;
   }
   f4 acc[NF][RMG];
-  C::template run<false>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, lb, P.d,
-                         (m + 15) >> 4);
+  C::template run<false, 64>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, lb, P.d,
+                             (m + 15) >> 4);
 #pragma unroll
   for (int a = 0; a < NF; ++a) {
 #pragma unroll
@@ -1021,9 +1035,8 @@ __device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i
   const float *sc[NF];
 #pragma unroll
   for (int a = 0; a < NH; ++a) {
-    const size_t rowoff = (size_t)(n0 + 16 * a + j) * P.d * wsz + g * 16;
-    wrow[a] = wgb + emat + rowoff;
-    wrow[a + NH] = wub + emat + rowoff;
+    wrow[a] = frag_ptr(wgb + emat, n0 + 16 * a, (size_t)P.d * wsz, lane);
+    wrow[a + NH] = frag_ptr(wub + emat, n0 + 16 * a, (size_t)P.d * wsz, lane);
     sc[a] = sc[a + NH] = nullptr;
     if constexpr (WT == WFP8) {
       const int nkb = P.d / 128;
@@ -1035,8 +1048,8 @@ __device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i
   f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
-  C::template run<false>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, lb, P.d,
-                         ngroups);
+  C::template run<false, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, lb,
+                                 P.d, ngroups);
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
 #pragma unroll
   for (int b = 0; b < MG; ++b) {
@@ -1086,8 +1099,7 @@ __device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm, const
   const float *sc[NF];
 #pragma unroll
   for (int a = 0; a < NF; ++a) {
-    const int rr = min(d0 + 16 * a + j, P.d - 1);
-    wrow[a] = wdb + emat + (size_t)rr * P.n * wsz + g * 16;
+    wrow[a] = frag_ptr(wdb + emat, min(d0 + 16 * a, P.d - 16), (size_t)P.n * wsz, lane);
     sc[a] = nullptr;
     if constexpr (WT == WFP8) {
       const int nkb = P.n / 128;
@@ -1098,8 +1110,8 @@ __device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm, const
   f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
-  C::template run<true>(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n * asz, sm.rows, lb, P.n,
-                        ngroups);
+  C::template run<true, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n * asz, sm.rows, lb,
+                                P.n, ngroups);
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
 #pragma unroll
   for (int b = 0; b < MG; ++b) {
@@ -1158,7 +1170,7 @@ __device__ __forceinline__ void stream_frags(f4 (&acc)[NFR], const char *const (
   uint4 wq[D][NFR], aq[D][NA];
   auto load_w = [&](int slot, int t) {
 #pragma unroll
-    for (int f = 0; f < NFR; ++f) wq[slot][f] = ld_stream16(t < nsteps ? w[f] + (size_t)t * 64 : wdummy);
+    for (int f = 0; f < NFR; ++f) wq[slot][f] = ld_stream16(t < nsteps ? w[f] + (size_t)t * kWStep : wdummy);
   };
 #pragma unroll
   for (int u = 0; u < D; ++u) {
@@ -1221,6 +1233,10 @@ template <int WT> __device__ __forceinline__ int act_lane_off(int g) {
   else return g * 16;                       // 16 bytes of the same element width
 }
 
+// gate/up unit (16-row m-tiles): 16 tokens x 16 H columns; waves 0/1 stream the 16 gate
+// rows, waves 2/3 the 16 up rows, each over one half of K; the four partial tiles meet in
+// LDS and wave 0 applies SwiGLU.  Shared-expert units need no routing, so they run in the
+// first phase, while the router and top-k items are still working.
 template <int WT, class SM>
 __device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i, SM &sm, bool deep) {
   constexpr int WSZ = Ty<WT>::WSZ, ASZ = Ty<WT>::ASZ, KU = Ty<WT>::KU;
@@ -1247,11 +1263,11 @@ __device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i
   // its first loads (stream_frag's mk_a), so the two latencies overlap
   const int slot = shared ? 0 : ld_coh(P.perm + row0 + rr);
   __builtin_amdgcn_sched_barrier(0);
-  // wave 0/1: gate rows, wave 2/3: up rows; K half wv & 1
   const int kh = P.d / 2, k0 = (wv & 1) * kh;
-  const char *wb = reinterpret_cast<const char *>(wv < 2 ? (shared ? P.shg : P.wg) : (shared ? P.shu : P.wu));
+  const void *wm = wv < 2 ? (shared ? P.shg : P.wg) : (shared ? P.shu : P.wu);
   const size_t emat = shared ? 0 : (size_t)e * P.n * P.d * WSZ;
-  const char *w = wb + emat + (size_t)(16 * s + j) * P.d * WSZ + (size_t)k0 * WSZ + g * 16;
+  const char *w = frag_ptr(reinterpret_cast<const char *>(wm) + emat, 16 * s, (size_t)P.d * WSZ, lane) +
+                  (size_t)(k0 * WSZ / 64) * kWStep;
   auto mk_a = [&]() {
     const int tok = min(max(shared ? row0 + rr : slot / P.k, 0), P.T - 1);
     return reinterpret_cast<const char *>(P.x) + ((size_t)tok * P.d + k0) * ASZ + act_lane_off<WT>(g);
@@ -1267,9 +1283,8 @@ __device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i
   f4 pa[1];
   if (deep) stream_frags<WT, false, 1, 8>(pa, wf, mk_a, KU * ASZ, kh / KU, sc);
   else stream_frags<WT, false, 1, 4>(pa, wf, mk_a, KU * ASZ, kh / KU, sc);
-  const f4 part = pa[0];
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
-  sm.u.red[wv][lane] = part;
+  sm.u.red[wv][lane] = pa[0];
   __syncthreads();
   if (wv == 0 && j < m) {
     const f4 gs = sm.u.red[0][lane] + sm.u.red[1][lane];
@@ -1282,6 +1297,7 @@ __device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i
   wg_signal(P.gudone + counter);
 }
 
+// down unit (16-row m-tiles): 64 output channels, 16 per wave, each over the whole of n
 template <int WT, class SM>
 __device__ __forceinline__ bool down_unit(const KParams &P, int i, SM &sm, bool deep) {
   constexpr int WSZ = Ty<WT>::WSZ, ASZ = Ty<WT>::ASZ, KU = Ty<WT>::KU;
@@ -1302,34 +1318,23 @@ __device__ __forceinline__ bool down_unit(const KParams &P, int i, SM &sm, bool 
     hrow0 = (size_t)uni(ds.y);
     m = uni(ds.z);
   }
-  constexpr int NFR = 1;
-  const int o0 = ob * (64 * NFR) + wv * 16 * NFR;  // this wave's 16 * NFR output channels
+  const int o0 = ob * 64 + wv * 16;  // this wave's 16 output channels
   const char *wb = reinterpret_cast<const char *>(shared ? P.shd : P.wd) + (shared ? 0 : (size_t)e * P.d * P.n * WSZ);
-  const char *w[NFR];
-#pragma unroll
-  for (int f = 0; f < NFR; ++f) w[f] = wb + (size_t)(o0 + 16 * f + j) * P.n * WSZ + g * 16;
+  const char *w[1] = {frag_ptr(wb, o0, (size_t)P.n * WSZ, lane)};
   auto mk_a = [&]() {
     return reinterpret_cast<const char *>(P.H) + (hrow0 + min(j, m - 1)) * (size_t)P.n * ASZ + act_lane_off<WT>(g);
   };
-  const float *sc[NFR];
-#pragma unroll
-  for (int f = 0; f < NFR; ++f) {
-    sc[f] = nullptr;
-    if constexpr (WT == WFP8) {
-      const int nkb = P.n / 128;
-      sc[f] = (shared ? P.shsd : P.sd) + (shared ? 0 : (size_t)e * (P.d / 128) * nkb) +
-              (size_t)((o0 + 16 * f) / 128) * nkb;
-    }
+  const float *sc[1] = {nullptr};
+  if constexpr (WT == WFP8) {
+    const int nkb = P.n / 128;
+    sc[0] = (shared ? P.shsd : P.sd) + (shared ? 0 : (size_t)e * (P.d / 128) * nkb) + (size_t)(o0 / 128) * nkb;
   }
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
-  f4 acc[NFR];
-  if (deep) stream_frags<WT, true, NFR, 8>(acc, w, mk_a, KU * ASZ, P.n / KU, sc);
-  else stream_frags<WT, true, NFR, 4>(acc, w, mk_a, KU * ASZ, P.n / KU, sc);
+  f4 acc[1];
+  if (deep) stream_frags<WT, true, 1, 8>(acc, w, mk_a, KU * ASZ, P.n / KU, sc);
+  else stream_frags<WT, true, 1, 4>(acc, w, mk_a, KU * ASZ, P.n / KU, sc);
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
-  if (j < m) {
-#pragma unroll
-    for (int f = 0; f < NFR; ++f) store4<WT>(P.Y, (hrow0 + j) * (size_t)P.d + o0 + 16 * f + 4 * g, acc[f]);
-  }
+  if (j < m) store4<WT>(P.Y, (hrow0 + j) * (size_t)P.d + o0 + 4 * g, acc[0]);
   wg_signal(P.ctrl + kSlotInts * C_DDONE);
   return true;
 }
@@ -1390,7 +1395,6 @@ __device__ __forceinline__ void combine_item(const KParams &P, int c) {
 // ---------------------------------------------------------------------------------
 // the persistent kernel
 // ---------------------------------------------------------------------------------
-enum ItemKind : int { K_ZERO = 0, K_ROUTER = 1, K_TOPK = 2, K_SHGU = 3, K_SCATTER = 4, K_GU = 5, K_DN = 6, K_COMB = 7 };
 
 // register budget per kernel (waves per SIMD): 2 for the narrow tiles, 1 for the widest
 template <int WT, int MG> struct Occ {
@@ -1484,30 +1488,28 @@ void moe_persistent(KParams P) {
       // memory system busy, else a shallow one (4 steps): with every wave of the grid
       // streaming, more requests in flight only add contention
       const bool deep = 2 * n_G <= kWaves * (int)gridDim.x;
-      if (i < n_G) {
+      if (i < n_G + n_D) {
         if (!scat_seen) {
           if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S, err, sm)) break;
           scat_seen = true;
         }
-        if (!zero_seen) {
+        if (!zero_seen) {  // the dependency counters must be cleared before they are used
           if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
           zero_seen = true;
         }
-        if constexpr (MG == 1) gateup_unit<WT>(P, false, i, sm, deep);
-        else gateup_item<WT, MG>(P, false, i, sm, lb);
-        kind = K_GU;
-      } else if ((i -= n_G) < n_D) {
-        if (!zero_seen) {  // the dependency counters must be cleared before they are read
-          if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
-          zero_seen = true;
-        }
-        if constexpr (MG == 1) {
-          if (!down_unit<WT>(P, i, sm, deep)) break;
+        if (i < n_G) {
+          if constexpr (MG == 1) gateup_unit<WT>(P, false, i, sm, deep);
+          else gateup_item<WT, MG>(P, false, i, sm, lb);
+          kind = K_GU;
         } else {
-          if (!down_item<WT, MG>(P, i, sm, lb)) break;
+          if constexpr (MG == 1) {
+            if (!down_unit<WT>(P, i - n_G, sm, deep)) break;
+          } else {
+            if (!down_item<WT, MG>(P, i - n_G, sm, lb)) break;
+          }
+          kind = K_DN;
         }
-        kind = K_DN;
-      } else if ((i -= n_D) < P.n_comb) {
+      } else if ((i -= n_G + n_D) < P.n_comb) {
         if (!dn_seen) {
           if (!wg_wait(ctrl + kSlotInts * C_DDONE, n_D, err, sm)) break;
           dn_seen = true;
@@ -1544,6 +1546,17 @@ void moe_persistent(KParams P) {
 __global__ void ws_init_kernel(int *ctrl, size_t nwords) {
   for (size_t q = blockIdx.x * (size_t)blockDim.x + threadIdx.x; q < nwords; q += (size_t)gridDim.x * blockDim.x)
     ctrl[q] = (q == (size_t)kSlotInts * C_MAGIC) ? kMagic : 0;
+}
+
+// row-major -> packed fragment layout of nmat matrices of [R rows, C bytes] (R % 16 == 0,
+// C % 64 == 0), contiguous in src and dst: one 16-byte chunk per thread, written in order
+__global__ void pack_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst, size_t nchunks, int C16) {
+  const size_t frag16 = (size_t)16 * C16;  // 16-byte chunks per fragment (16 rows)
+  for (size_t q = blockIdx.x * (size_t)blockDim.x + threadIdx.x; q < nchunks; q += (size_t)gridDim.x * blockDim.x) {
+    const size_t f = q / frag16, rem = q % frag16;
+    const int s = (int)(rem >> 6), l = (int)(rem & 63), j = l & 15, g = l >> 4;
+    dst[q] = src[(f * 16 + j) * C16 + 4 * s + g];
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -1794,6 +1807,7 @@ moe_status moe_forward_ex(const moe_problem *p, const void *hidden, const void *
   if (!hidden || !w_router || !out) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(hidden) || !aligned16(w_router) || !aligned16(out)) return MOE_ERR_INVALID_ARGUMENT;
   if (out == hidden) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->w_layout != MOE_W_PACKED) return MOE_ERR_UNSUPPORTED;  // see moe_pack_weights
   st = check_weights(p, w);
   if (st != MOE_OK) return st;
   Call c{};
@@ -1824,6 +1838,47 @@ moe_status moe_forward(const moe_problem *p, const void *hidden, const void *w_r
                        const moe_weights *w, void *out, const moe_route_out *ro, void *ws, size_t ws_bytes,
                        hipStream_t stream) {
   return moe_forward_ex(p, hidden, w_router, bias, w, out, ro, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_pack_weights(const moe_problem *p, const moe_weights *src, const moe_weights *dst,
+                            hipStream_t stream) {
+  if (!p) return MOE_ERR_INVALID_ARGUMENT;
+  moe_problem q = *p;
+  q.w_layout = MOE_W_ROWMAJOR;
+  moe_status st = validate_problem(&q);
+  if (st != MOE_OK) return st;
+  if (!src || !dst) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t wsz = dtype_size(p->w_dtype);
+  struct Job {
+    const void *s;
+    void *d;
+    size_t nmat, rows, cols_bytes;
+  } jobs[6] = {
+      {src->w_gate, const_cast<void *>(dst->w_gate), (size_t)p->E, (size_t)p->n, (size_t)p->d * wsz},
+      {src->w_up, const_cast<void *>(dst->w_up), (size_t)p->E, (size_t)p->n, (size_t)p->d * wsz},
+      {src->w_down, const_cast<void *>(dst->w_down), (size_t)p->E, (size_t)p->d, (size_t)p->n * wsz},
+      {src->sh_gate, const_cast<void *>(dst->sh_gate), 1, (size_t)p->n, (size_t)p->d * wsz},
+      {src->sh_up, const_cast<void *>(dst->sh_up), 1, (size_t)p->n, (size_t)p->d * wsz},
+      {src->sh_down, const_cast<void *>(dst->sh_down), 1, (size_t)p->d, (size_t)p->n * wsz},
+  };
+  const int njobs = p->n_shared ? 6 : 3;
+  for (int i = 0; i < njobs; ++i) {
+    const Job &J = jobs[i];
+    if (!J.s || !J.d || !aligned16(J.s) || !aligned16(J.d)) return MOE_ERR_INVALID_ARGUMENT;
+    const size_t bytes = J.nmat * J.rows * J.cols_bytes;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(J.s), b = reinterpret_cast<uintptr_t>(J.d);
+    if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARGUMENT;  // overlap
+  }
+  for (int i = 0; i < njobs; ++i) {
+    const Job &J = jobs[i];
+    const size_t nchunks = J.nmat * J.rows * J.cols_bytes / 16;
+    size_t blocks = (nchunks + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const uint4 *>(J.s),
+                       static_cast<uint4 *>(J.d), nchunks, (int)(J.cols_bytes / 16));
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
 }
 
 moe_status moe_last_device_error(const void *ws, hipStream_t stream) {

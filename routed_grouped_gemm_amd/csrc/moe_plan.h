@@ -88,6 +88,7 @@ inline moe_status validate_problem(const moe_problem *p) {
   } else if (p->scale_block != 0) {
     return MOE_ERR_INVALID_ARGUMENT;
   }
+  if (p->w_layout != MOE_W_ROWMAJOR && p->w_layout != MOE_W_PACKED) return MOE_ERR_INVALID_ARGUMENT;
   if (p->E > kMaxE || p->k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (p->d % 256 || p->n % 256) return MOE_ERR_UNSUPPORTED;
   if (p->T * (int64_t)p->k >= (int64_t(1) << 31) - 1) return MOE_ERR_UNSUPPORTED;

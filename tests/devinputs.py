@@ -26,11 +26,15 @@ WEIGHT_KEYS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate"
                "sh_s_gate", "sh_s_up", "sh_s_down")
 
 
-def to_device(inp, device="cuda"):
-    """Returns (problem, hidden, w_router, bias, weights dict) on the device."""
+def to_device(inp, device="cuda", layout="packed"):
+    """Returns (problem, hidden, w_router, bias, weights dict) on the device.  layout
+    "packed" converts the expert matrices with the library's moe_pack_weights (the
+    problem then says so); "rowmajor" passes them as generated."""
     c = inp.cfg
-    p = moe.problem(c["T"], c["d"], c["n"], c["E"], c["k"], c["shared"], c["act"], c["w"])
+    p = moe.problem(c["T"], c["d"], c["n"], c["E"], c["k"], c["shared"], c["act"], c["w"], layout=layout)
     weights = {k: tensor(getattr(inp, k), device) for k in WEIGHT_KEYS if getattr(inp, k) is not None}
+    if layout == "packed":
+        weights = moe.pack_weights(p, weights)  # the row-major copies are released here
     return p, tensor(inp.hidden, device), tensor(inp.w_router, device), tensor(inp.bias, device), weights
 
 

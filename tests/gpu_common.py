@@ -20,8 +20,8 @@ def require_gpu():
         build.build()
 
 
-def run_forward(inp, **kw):
-    p, x, wr, b, W = to_device(inp)
+def run_forward(inp, layout="packed", **kw):
+    p, x, wr, b, W = to_device(inp, layout=layout)
     ws = moe.alloc_workspace(p)
     out, r = moe.forward(p, x, wr, b, W, ws, route_out=True, **kw)
     torch.cuda.synchronize()
@@ -92,10 +92,10 @@ def oracle_reference(v, L, ids, gids, mism, tokens=None):
     return ref
 
 
-def full_parity(inp, tol=None, **kw):
+def full_parity(inp, tol=None, layout="packed", **kw):
     c = inp.cfg
     tol = tol if tol is not None else TOL[c["w"]]
-    out, r, ctx = run_forward(inp, **kw)
+    out, r, ctx = run_forward(inp, layout=layout, **kw)
     v = oracle.InputsView(inp)
     L, ids, gids, mism = check_routing(v, r, c["k"], c["E"])
     check_permutation(r, c["k"], c["E"])

@@ -27,7 +27,7 @@ def test_exports_every_header_function(L):
 
 
 def test_version_and_strings(L):
-    assert moe.abi_version() == 1
+    assert moe.abi_version() == 2
     for code, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARGUMENT"), (2, "MOE_ERR_UNSUPPORTED"),
                        (3, "MOE_ERR_WORKSPACE_TOO_SMALL"), (4, "MOE_ERR_HIP"), (5, "MOE_ERR_DEVICE_FAULT")]:
         assert moe.status_string(code) == name
@@ -69,6 +69,45 @@ def test_workspace_size_monotone_in_T(L):
     assert sizes[-1] > 4096 * 8 * (512 + 2048) * 2
 
 
+def test_weight_layout_rules(L):
+    assert ws_size(moe.problem(16, 2048, 512, 256, 8, layout="packed"))[0] == 0
+    p = moe.problem(16, 2048, 512, 256, 8)
+    p.w_layout = 2
+    assert ws_size(p)[0] == INVALID
+    # the forward reads packed weights only; row-major ones are refused before any launch
+    VP = ctypes.c_void_p
+    fake = VP(1 << 20)
+    W = moe.Weights(*([1 << 21] * 3 + [None] * 9))
+    rm = moe.problem(16, 2048, 512, 256, 8, layout="rowmajor")
+    assert L.moe_forward(ctypes.byref(rm), fake, fake, None, ctypes.byref(W), VP(3 << 20), None, fake, 1 << 30,
+                         None) == UNSUPPORTED
+
+
+def test_pack_weights_rejects_bad_arguments_before_launch(L):
+    """moe_pack_weights validates everything on the host (no HIP call on these paths)."""
+    VP = ctypes.c_void_p
+    p = moe.problem(16, 2048, 512, 256, 8)
+    nbytes = 256 * 512 * 2048 * 2
+    src = moe.Weights(*([1 << 40, (1 << 40) + nbytes, (1 << 40) + 2 * nbytes] + [None] * 9))
+    dst = moe.Weights(*([1 << 41, (1 << 41) + nbytes, (1 << 41) + 2 * nbytes] + [None] * 9))
+    assert L.moe_pack_weights(None, ctypes.byref(src), ctypes.byref(dst), None) == INVALID
+    assert L.moe_pack_weights(ctypes.byref(p), None, ctypes.byref(dst), None) == INVALID
+    assert L.moe_pack_weights(ctypes.byref(p), ctypes.byref(src), None, None) == INVALID
+    # a missing matrix, a misaligned one, and a destination that overlaps its source
+    miss = moe.Weights(*([1 << 41, None, (1 << 41) + 2 * nbytes] + [None] * 9))
+    assert L.moe_pack_weights(ctypes.byref(p), ctypes.byref(src), ctypes.byref(miss), None) == INVALID
+    odd = moe.Weights(*([(1 << 41) + 8, (1 << 41) + nbytes, (1 << 41) + 2 * nbytes] + [None] * 9))
+    assert L.moe_pack_weights(ctypes.byref(p), ctypes.byref(src), ctypes.byref(odd), None) == INVALID
+    lap = moe.Weights(*([(1 << 40) + 4096, (1 << 41) + nbytes, (1 << 41) + 2 * nbytes] + [None] * 9))
+    assert L.moe_pack_weights(ctypes.byref(p), ctypes.byref(src), ctypes.byref(lap), None) == INVALID
+    # the shared expert's matrices are required when the problem has one
+    ps = moe.problem(16, 2048, 512, 256, 8, n_shared=1)
+    assert L.moe_pack_weights(ctypes.byref(ps), ctypes.byref(src), ctypes.byref(dst), None) == INVALID
+    # shapes are validated like the compute calls
+    bad = moe.problem(16, 2000, 512, 256, 8)
+    assert L.moe_pack_weights(ctypes.byref(bad), ctypes.byref(src), ctypes.byref(dst), None) == UNSUPPORTED
+
+
 def test_scale_block_rules(L):
     p = moe.problem(4, 256, 256, 4, 2, w="fp8")
     p.scale_block = 64
@@ -80,7 +119,7 @@ def test_scale_block_rules(L):
 
 def test_compute_calls_reject_bad_arguments_before_launch(L):
     """Host-side validation returns before any HIP call, so this runs without a GPU."""
-    p = moe.problem(16, 2048, 512, 256, 8)
+    p = moe.problem(16, 2048, 512, 256, 8, layout="packed")
     W = moe.Weights()
     VP = ctypes.c_void_p
     fake = VP(1 << 20)  # never dereferenced: validation fails first
@@ -100,10 +139,10 @@ def test_compute_calls_reject_bad_arguments_before_launch(L):
     rc = L.moe_forward(ctypes.byref(p), fake, fake, None, ctypes.byref(W2), VP(3 << 20), None, VP((1 << 20) + 16), 1 << 30, None)
     assert rc == INVALID
     # fp8 without scales
-    p8 = moe.problem(4, 256, 256, 4, 2, w="fp8")
+    p8 = moe.problem(4, 256, 256, 4, 2, w="fp8", layout="packed")
     assert L.moe_forward(ctypes.byref(p8), fake, fake, None, ctypes.byref(W2), VP(3 << 20), None, fake, 1 << 30, None) == INVALID
     # shared expert requested but missing
-    ps = moe.problem(4, 256, 256, 4, 2, n_shared=1)
+    ps = moe.problem(4, 256, 256, 4, 2, n_shared=1, layout="packed")
     assert L.moe_forward(ctypes.byref(ps), fake, fake, None, ctypes.byref(W2), VP(3 << 20), None, fake, 1 << 30, None) == INVALID
     # route/permute argument checks
     assert L.moe_route(ctypes.byref(p), fake, fake, None, None, fake, None, fake, 1 << 30, None) == INVALID

@@ -43,7 +43,7 @@ def test_large_fp8_forward(large, T):
                           s_gate=inp_full.s_gate, s_up=inp_full.s_up, s_down=inp_full.s_down,
                           sh_gate=inp_full.sh_gate, sh_up=inp_full.sh_up, sh_down=inp_full.sh_down,
                           sh_s_gate=inp_full.sh_s_gate, sh_s_up=inp_full.sh_s_up, sh_s_down=inp_full.sh_s_down)
-    p = moe.problem(T, cfg["d"], cfg["n"], cfg["E"], cfg["k"], 1, "bf16", "fp8")
+    p = moe.problem(T, cfg["d"], cfg["n"], cfg["E"], cfg["k"], 1, "bf16", "fp8", layout="packed")
     x = x_full[:T].contiguous()
     ws = moe.alloc_workspace(p)
     out, r = moe.forward(p, x, wr, b, W, ws, route_out=True)

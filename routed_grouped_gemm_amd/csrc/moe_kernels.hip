@@ -95,6 +95,7 @@ struct KParams {
   float *wts;
   int *counts, *offsets, *perm, *inv_perm;
   int *ctrl, *gudone, *hist, *mtoff;
+  int *mtok;      // 16-row m-tiles: token of each row, m-tile-major (rows past the end: stale)
   int4 *desc;
   void *H, *Y;
   unsigned long long *trace;
@@ -766,10 +767,12 @@ __device__ __forceinline__ void chunk_masks(const KParams &P, int ntok, SM &sm) 
 
 // stable scatter of a chunk: slot (t, j) with expert e goes to
 //   offsets[e] + base[e] + #(earlier tokens of the chunk that chose e)
-// (a token chooses an expert at most once, so the rank is a popcount of the mask)
+// (a token chooses an expert at most once, so the rank is a popcount of the mask).
+// mto (16-row m-tiles): per-expert m-tile offsets; the slot's token is also written to the
+// m-tile token table (row r of expert e's rows: m-tile mto[e] + r / 16, row r % 16)
 template <class SM>
 __device__ __forceinline__ void chunk_scatter(const KParams &P, int c, int ntok, const int *offs, const int *base,
-                                              SM &sm) {
+                                              const int *mto, SM &sm) {
   const int tid = otid(), k = P.k, E = P.E, t0 = c * P.tk;
   for (int q = tid; q < ntok * k; q += kThreads) {
     const int e = sm.u.r.ids[q];
@@ -782,10 +785,11 @@ __device__ __forceinline__ void chunk_scatter(const KParams &P, int c, int ntok,
       if (w < (tt >> 5)) rank += __popc(mw);
       else if (w == (tt >> 5)) rank += __popc(mw & ((1u << (tt & 31)) - 1u));
     }
-    const int p = offs[e] + (base ? base[e] : 0) + rank;
+    const int r = (base ? base[e] : 0) + rank, p = offs[e] + r;
     const int slot = t0 * k + q;
     st_coh(P.perm + p, slot);
     st_coh(P.inv_perm + slot, p);
+    if (mto) st_coh(P.mtok + (mto[e] + (r >> 4)) * 16 + (r & 15), t0 + tt);
   }
 }
 
@@ -937,7 +941,7 @@ __device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
   if (P.n_kt == 1) {
     plan_wg(P, sm, true);
     __syncthreads();
-    chunk_scatter(P, 0, ntok, sm.u.r.scan0, nullptr, sm);
+    chunk_scatter(P, 0, ntok, sm.u.r.scan0, nullptr, P.bm == 16 ? sm.u.r.scan1 : nullptr, sm);
     wg_signal(P.ctrl + kSlotInts * C_KDONE);
     if (otid() == 0) __hip_atomic_fetch_add(P.ctrl + kSlotInts * C_PLAN, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
@@ -975,9 +979,10 @@ __device__ __forceinline__ void scatter_item(const KParams &P, int c, SM &sm) {
   for (int e = tid; e < E; e += kThreads) {
     sm.u.r.scan0[e] = ld_coh(P.offsets + e);
     sm.u.r.scan1[e] = ld_coh(P.hist + (size_t)c * E + e);
+    if (P.bm == 16) sm.u.r.tmp[e] = ld_coh(P.mtoff + e);
   }
   __syncthreads();
-  chunk_scatter(P, c, ntok, sm.u.r.scan0, sm.u.r.scan1, sm);
+  chunk_scatter(P, c, ntok, sm.u.r.scan0, sm.u.r.scan1, P.bm == 16 ? sm.u.r.tmp : nullptr, sm);
 }
 
 template <int WT> struct ActT { using type = uint16_t; };
@@ -1242,7 +1247,7 @@ __device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i
   constexpr int WSZ = Ty<WT>::WSZ, ASZ = Ty<WT>::ASZ, KU = Ty<WT>::KU;
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int gm = i / P.nt_gu, s = i % P.nt_gu;
-  int e, row0, m, counter;
+  int e, row0, m, counter, tokr = 0;
   size_t hrow0;
   if (shared) {
     e = P.E;
@@ -1251,7 +1256,11 @@ __device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i
     hrow0 = (size_t)P.T * P.k + row0;
     counter = gm;
   } else {
+    // the descriptor and the m-tile's token ids are independent loads (one round trip);
+    // the token is consumed after the first weight loads are issued (stream_frag's mk_a)
     const int4 ds = ld_coh_int4(P.desc + gm);
+    tokr = ld_coh(P.mtok + gm * 16 + j);
+    __builtin_amdgcn_sched_barrier(0);
     e = uni(ds.x);
     row0 = uni(ds.y);
     m = uni(ds.z);
@@ -1259,17 +1268,13 @@ __device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i
     counter = P.n_shmt + gm;
   }
   const int rr = min(j, m - 1);
-  // the permutation lookup is issued before the weight stream starts and consumed after
-  // its first loads (stream_frag's mk_a), so the two latencies overlap
-  const int slot = shared ? 0 : ld_coh(P.perm + row0 + rr);
-  __builtin_amdgcn_sched_barrier(0);
   const int kh = P.d / 2, k0 = (wv & 1) * kh;
   const void *wm = wv < 2 ? (shared ? P.shg : P.wg) : (shared ? P.shu : P.wu);
   const size_t emat = shared ? 0 : (size_t)e * P.n * P.d * WSZ;
   const char *w = frag_ptr(reinterpret_cast<const char *>(wm) + emat, 16 * s, (size_t)P.d * WSZ, lane) +
                   (size_t)(k0 * WSZ / 64) * kWStep;
   auto mk_a = [&]() {
-    const int tok = min(max(shared ? row0 + rr : slot / P.k, 0), P.T - 1);
+    const int tok = min(max(shared ? row0 + rr : tokr, 0), P.T - 1);
     return reinterpret_cast<const char *>(P.x) + ((size_t)tok * P.d + k0) * ASZ + act_lane_off<WT>(g);
   };
   const float *sc[1] = {nullptr};
@@ -1297,7 +1302,8 @@ __device__ __forceinline__ void gateup_unit(const KParams &P, bool shared, int i
   wg_signal(P.gudone + counter);
 }
 
-// down unit (16-row m-tiles): 64 output channels, 16 per wave, each over the whole of n
+// down unit (16-row m-tiles): 128 output channels; each wave streams two adjacent 16-row
+// fragments (32 channels, one contiguous stretch of the packed matrix) over the whole of n
 template <int WT, class SM>
 __device__ __forceinline__ bool down_unit(const KParams &P, int i, SM &sm, bool deep) {
   constexpr int WSZ = Ty<WT>::WSZ, ASZ = Ty<WT>::ASZ, KU = Ty<WT>::KU;
@@ -1318,23 +1324,25 @@ __device__ __forceinline__ bool down_unit(const KParams &P, int i, SM &sm, bool 
     hrow0 = (size_t)uni(ds.y);
     m = uni(ds.z);
   }
-  const int o0 = ob * 64 + wv * 16;  // this wave's 16 output channels
+  const int o0 = ob * 128 + wv * 32;  // this wave's 32 output channels
   const char *wb = reinterpret_cast<const char *>(shared ? P.shd : P.wd) + (shared ? 0 : (size_t)e * P.d * P.n * WSZ);
-  const char *w[1] = {frag_ptr(wb, o0, (size_t)P.n * WSZ, lane)};
+  const char *w[2] = {frag_ptr(wb, o0, (size_t)P.n * WSZ, lane), frag_ptr(wb, o0 + 16, (size_t)P.n * WSZ, lane)};
   auto mk_a = [&]() {
     return reinterpret_cast<const char *>(P.H) + (hrow0 + min(j, m - 1)) * (size_t)P.n * ASZ + act_lane_off<WT>(g);
   };
-  const float *sc[1] = {nullptr};
+  const float *sc[2] = {nullptr, nullptr};
   if constexpr (WT == WFP8) {
     const int nkb = P.n / 128;
-    sc[0] = (shared ? P.shsd : P.sd) + (shared ? 0 : (size_t)e * (P.d / 128) * nkb) + (size_t)(o0 / 128) * nkb;
+    sc[0] = sc[1] = (shared ? P.shsd : P.sd) + (shared ? 0 : (size_t)e * (P.d / 128) * nkb) + (size_t)(o0 / 128) * nkb;
   }
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
-  f4 acc[1];
-  if (deep) stream_frags<WT, true, 1, 8>(acc, w, mk_a, KU * ASZ, P.n / KU, sc);
-  else stream_frags<WT, true, 1, 4>(acc, w, mk_a, KU * ASZ, P.n / KU, sc);
+  f4 acc[2];
+  stream_frags<WT, true, 2, 4>(acc, w, mk_a, KU * ASZ, P.n / KU, sc);
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
-  if (j < m) store4<WT>(P.Y, (hrow0 + j) * (size_t)P.d + o0 + 4 * g, acc[0]);
+  if (j < m) {
+    store4<WT>(P.Y, (hrow0 + j) * (size_t)P.d + o0 + 4 * g, acc[0]);
+    store4<WT>(P.Y, (hrow0 + j) * (size_t)P.d + o0 + 16 + 4 * g, acc[1]);
+  }
   wg_signal(P.ctrl + kSlotInts * C_DDONE);
   return true;
 }
@@ -1695,6 +1703,7 @@ moe_status launch(const Call &c) {
   P.desc = reinterpret_cast<int4 *>(ws + L.off_desc);
   P.hist = reinterpret_cast<int *>(ws + L.off_hist);
   P.mtoff = reinterpret_cast<int *>(ws + L.off_mtoff);
+  P.mtok = reinterpret_cast<int *>(ws + L.off_mtok);
   P.H = ws + L.off_h;
   P.Y = ws + L.off_y;
   if (c.opts && c.opts->trace) {

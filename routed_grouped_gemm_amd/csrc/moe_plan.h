@@ -45,7 +45,7 @@ struct Tiles {
   int bm;          // rows per m-tile = 16 * mg
   int nf;          // 16-row weight fragments per wave (2 when mg == 1, else 4)
   int gu_cols;     // H columns per gate/up item: 4 waves x nf/2 x 16 (16 when mg == 1)
-  int dn_cols;     // output columns per down item: 4 waves x nf x 16 (64 when mg == 1)
+  int dn_cols;     // output columns per down item: 4 waves x nf x 16 (128 when mg == 1)
   int tk;          // tokens per scatter chunk (tk <= 128, tk * k <= 1024)
   int rt_tokens;   // router item: tokens x experts (16 x 16 split over the 4 waves when
   int rt_experts;  //   mg == 1, else 16 x 128 on the 16-row expert tile core)
@@ -65,7 +65,7 @@ struct Layout {
   int64_t rows_h;        // rows of H and Y: T*k + n_shared*T
   // byte offsets into the workspace
   size_t off_gudone, off_desc, off_logits, off_ids, off_wts, off_hist, off_counts, off_offsets, off_mtoff,
-      off_perm, off_invperm, off_h, off_y, total;
+      off_perm, off_invperm, off_mtok, off_h, off_y, total;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -105,9 +105,9 @@ inline Tiles choose_tiles(const moe_problem *p) {
   t.bm = 16 * t.mg;
   t.nf = t.mg == 1 ? 2 : 4;
   // mg == 1: small units streamed by single waves (gate/up: 16 columns, the waves split
-  // gate/up and the two halves of K; down: 16 channels per wave)
+  // gate/up and the two halves of K; down: 32 channels per wave)
   t.gu_cols = t.mg == 1 ? 16 : 4 * (t.nf / 2) * 16;
-  t.dn_cols = t.mg == 1 ? 64 : 4 * t.nf * 16;
+  t.dn_cols = t.mg == 1 ? 128 : 4 * t.nf * 16;
   t.tk = kMaxChunkSlots / p->k;
   if (t.tk > kMaxChunkTokens) t.tk = kMaxChunkTokens;
   if (t.tk < 1) t.tk = 1;
@@ -163,6 +163,7 @@ inline Layout make_layout(const moe_problem *p) {
   L.off_mtoff = take(sizeof(int32_t) * (size_t)(E + 1));
   L.off_perm = take(sizeof(int32_t) * (size_t)tk);
   L.off_invperm = take(sizeof(int32_t) * (size_t)tk);
+  L.off_mtok = take(sizeof(int32_t) * (bm == 16 ? (size_t)L.mt_routed_max * 16 : 16));
   L.off_h = take(asz * (size_t)L.rows_h * (size_t)p->n);
   L.off_y = take(asz * (size_t)L.rows_h * (size_t)p->d);
   L.total = o;

@@ -152,7 +152,7 @@ typedef struct {
 moe_status moe_workspace_size(const moe_problem *p, size_t *bytes /* (host) out */);
 
 /* Clears the workspace's control block (a fill kernel on `stream`).  Call once after
- * allocating a workspace, and again after a MOE_ERR_DEVICE_FAULT.  Needs at least 65536
+ * allocating a workspace, and again after a MOE_ERR_DEVICE_FAULT.  Needs at least 131072
  * bytes. */
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 

@@ -566,11 +566,15 @@ __device__ __forceinline__ void zero_item(const KParams &P, int i) {
 }
 
 // router logits, decode-sized tiles: 16 tokens x 16 experts; wave w sums the K range
-// [w*d/4, (w+1)*d/4), then the four partial sums are added in wave order
+// [w*d/4, (w+1)*d/4), then the four partial sums are added in wave order.  Latency matters
+// here (the rest of the layer waits for the routing), so each wave issues all of its loads
+// of a 16-step chunk (and the bias) before the first MFMA: one memory round trip per chunk.
+// Steps past the end read the last step again and multiply zero activations.
 template <int WT, class SM>
 __device__ __forceinline__ void logits_item_split(const KParams &P, int i, SM &sm) {
   constexpr int RT = (WT == WF32) ? WF32 : WBF16;  // the router runs in the activation dtype
   constexpr int KU = Ty<RT>::KU, ASZ = Ty<RT>::ASZ;
+  constexpr int CH = 16;  // K steps per chunk
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int lt = i / P.n_le, le = i % P.n_le;
   const int t0 = lt * 16, e0 = le * 16;
@@ -578,19 +582,28 @@ __device__ __forceinline__ void logits_item_split(const KParams &P, int i, SM &s
   const int er = min(e0 + j, P.E - 1), tr = min(t0 + j, P.T - 1);
   const char *wp = reinterpret_cast<const char *>(P.wr) + ((size_t)er * P.d + kbeg) * ASZ + g * 16;
   const char *xp = reinterpret_cast<const char *>(P.x) + ((size_t)tr * P.d + kbeg) * ASZ + g * 16;
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (P.bias) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bias[r] = P.bias[min(e0 + 4 * g + r, P.E - 1)];
+  }
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
   const int nsteps = kq / KU;
-  for (int s0 = 0; s0 < nsteps; s0 += 16) {
-    uint4 w[16], a[16];
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+  for (int s0 = 0; s0 < nsteps; s0 += CH) {
+    uint4 w[CH], a[CH];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int st = min(s0 + u, nsteps - 1);
-      w[u] = *reinterpret_cast<const uint4 *>(wp + (size_t)st * 64);
-      a[u] = *reinterpret_cast<const uint4 *>(xp + (size_t)st * 64);
+    for (int u = 0; u < CH; ++u) {
+      const size_t off = (size_t)min(s0 + u, nsteps - 1) * 64;
+      w[u] = ld_glob16(wp + off);
+      a[u] = ld_glob16(xp + off);
     }
+    asm volatile("" ::: "memory");  // every load of the chunk is in flight before the first MFMA
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (s0 + u < nsteps) acc = mfma_step<RT>(w[u], a[u], a[u], acc);
+    for (int u = 0; u < CH; ++u) {
+      const uint4 av = s0 + u < nsteps ? a[u] : z4;
+      acc = mfma_step<RT>(w[u], av, av, acc);
+    }
   }
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
   sm.u.red[wv][lane] = acc;
@@ -603,7 +616,7 @@ __device__ __forceinline__ void logits_item_split(const KParams &P, int i, SM &s
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int e = e0 + 4 * g + r;
-        if (e < P.E) st_coh(P.logits + (size_t)t * P.E + e, sum[r] + (P.bias ? P.bias[e] : 0.f));
+        if (e < P.E) st_coh(P.logits + (size_t)t * P.E + e, sum[r] + bias[r]);
       }
     }
   }
@@ -1420,7 +1433,9 @@ void moe_persistent(KParams P) {
   const int tid = threadIdx.x;
   int *ctrl = P.ctrl;
   int *err = ctrl + kSlotInts * C_ERR;
-  if (ld_relaxed(ctrl + kSlotInts * C_MAGIC) != kMagic) {
+  // (a plain load: the magic word only changes between launches, and a cached read keeps
+  // the whole grid from converging on one address at start-up)
+  if (*reinterpret_cast<const volatile int *>(ctrl + kSlotInts * C_MAGIC) != kMagic) {
     if (tid == 0) __hip_atomic_store(err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
@@ -1429,19 +1444,30 @@ void moe_persistent(KParams P) {
   bool zero_seen = false, logits_seen = false, plan_seen = false, scat_seen = false, dn_seen = false;
   int n_mt = -1;
   int step = 0;
-  int next = 0;
   const bool dynamic = P.schedule == 0;
-  if (dynamic && tid == 0) next = __hip_atomic_fetch_add(ctrl + kSlotInts * C_TICKET, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Dynamic tickets come from np = min(kTicketParts, grid) counters, one per partition of
+  // the workgroups (blockIdx % np): partition p hands out the tickets p, p + np, ... in
+  // order (every partition has a workgroup, so every ticket has a taker).  Device atomics on one address serialise (~11 ns each), and every workgroup takes
+  // a ticket at start-up and one per item: split over the partitions, neither the start-up
+  // burst nor the steady stream of ticket atomics queues up behind one address.  A ticket is
+  // still only ever taken by a running workgroup, and each partition's workgroups take their
+  // tickets in increasing order while waiting only for smaller tickets, so every wait ends
+  // (induction over the tickets, as with one counter).  Thread 0 keeps the next ticket
+  // prefetched, so the atomic's latency overlaps the current item.
+  const int nparts = min(kTicketParts, (int)gridDim.x), part = (int)blockIdx.x % nparts;
+  int *pctr = ctrl + kSlotInts * (C_PTICKET + part);
+  int next = 0;
+  if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (;;) {
     __syncthreads();
     if (dynamic) {
-      if (tid == 0) sm.bcast[0] = next;
+      if (tid == 0) sm.bcast[0] = part + nparts * next;
       __syncthreads();
     }
     const int ticket = dynamic ? uni(sm.bcast[0]) : (int)blockIdx.x + step * (int)gridDim.x;
     ++step;
     // prefetch the next ticket; its value is read at the top of the next iteration
-    if (dynamic && tid == 0) next = __hip_atomic_fetch_add(ctrl + kSlotInts * C_TICKET, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t t_start = P.trace ? wall_clock64() : 0;
     if (P.trace && tid == 0) sm.mark[0] = sm.mark[1] = 0;
     int kind = -1;
@@ -1546,6 +1572,7 @@ void moe_persistent(KParams P) {
     const int old = __hip_atomic_fetch_add(ctrl + kSlotInts * C_EXIT, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (int)gridDim.x - 1) {
       for (int s = C_TICKET; s <= C_NMT; ++s) ctrl[kSlotInts * s] = 0;
+      for (int q = 0; q < kTicketParts; ++q) ctrl[kSlotInts * (C_PTICKET + q)] = 0;
       __threadfence();
     }
   }

@@ -19,7 +19,9 @@ namespace {
 constexpr int kThreads = 256;          // threads per workgroup (4 wave64)
 constexpr int kWaves = 4;
 constexpr int kSlotInts = 1024;        // control slots sit 4 KB apart (separate HBM channels)
-constexpr int kCtrlBytes = 16 * kSlotInts * 4;  // control block at the start of the workspace
+constexpr int kCtrlSlots = 32;
+constexpr int kCtrlBytes = kCtrlSlots * kSlotInts * 4;  // control block at the start of the workspace
+constexpr int kTicketParts = 8;        // ticket counters (see C_PTICKET)
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 256;
 constexpr int kTopkTokens = 16;        // tokens per top-k item (4 per wave)
@@ -30,10 +32,12 @@ constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroin
 
 
 // control-block slots (one int32 each, at int index slot * kSlotInts): a poll of one
-// counter never shares a cache line or channel with the ticket counter or another counter
+// counter never shares a cache line or channel with the ticket counter or another counter.
+// C_PTICKET + p (p < kTicketParts): ticket counter of partition p (the workgroups with
+// blockIdx % kTicketParts == p), see the persistent kernel; C_TICKET is unused.
 enum CtrlSlot : int {
   C_MAGIC = 0, C_TICKET = 1, C_ZDONE = 2, C_LDONE = 3, C_KDONE = 4, C_PLAN = 5, C_SDONE = 6,
-  C_DDONE = 7, C_EXIT = 8, C_NMT = 9, C_ERR = 10, C_NSLOTS = 16
+  C_DDONE = 7, C_EXIT = 8, C_NMT = 9, C_ERR = 10, C_PTICKET = 16, C_NSLOTS = kCtrlSlots
 };
 constexpr int kMagic = 0x4d6f4531;     // "MoE1"
 

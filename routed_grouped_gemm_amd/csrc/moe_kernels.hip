@@ -1360,46 +1360,51 @@ __device__ __forceinline__ bool down_unit(const KParams &P, int i, SM &sm, bool 
   return true;
 }
 
-// combine: out[t] = sum_j w[t,j] * Y[inv_perm[t*k+j]] (+ Y[T*k + t]), float32, slot order
+// combine: out[t] = sum_j w[t,j] * Y[inv_perm[t*k+j]] (+ Y[T*k + t]), float32, slot order.
+// It runs after the last down unit, so its latency is the layer's tail: the slots are taken
+// 8 at a time, with all of their weights and row indices loaded first, then all 8 rows of Y.
 template <int WT>
 __device__ __forceinline__ void combine_item(const KParams &P, int c) {
   using A = typename ActT<WT>::type;
   constexpr int VEC = 16 / sizeof(A);
+  constexpr int SB = 8;  // slots per batch
   const int t0 = c * kCombineTokens, ntok = min(kCombineTokens, P.T - t0);
-  const int nv = P.d / VEC;
+  const int nv = P.d / VEC, k = P.k;
   const A *Y = reinterpret_cast<const A *>(P.Y);
   A *out = reinterpret_cast<A *>(P.out);
+  auto add = [&](float (&acc)[VEC], const uint4 &raw, float w) {
+    if constexpr (WT == WF32) {
+      const float *f = reinterpret_cast<const float *>(&raw);
+#pragma unroll
+      for (int z = 0; z < VEC; ++z) acc[z] += w * f[z];
+    } else {
+      const uint16_t *h = reinterpret_cast<const uint16_t *>(&raw);
+#pragma unroll
+      for (int z = 0; z < VEC; ++z) acc[z] += w * bf2f(h[z]);
+    }
+  };
   for (int q = otid(); q < ntok * nv; q += kThreads) {
     const int t = t0 + q / nv, v = q % nv;
     float acc[VEC];
 #pragma unroll
     for (int z = 0; z < VEC; ++z) acc[z] = 0.f;
-    for (int jj = 0; jj < P.k; ++jj) {
-      const float w = ld_coh(P.wts + (size_t)t * P.k + jj);
-      const int p = ld_coh(P.inv_perm + (size_t)t * P.k + jj);
-      const uint4 raw = ld_coh16(Y + (size_t)p * P.d + v * VEC);
-      if constexpr (WT == WF32) {
-        const float *f = reinterpret_cast<const float *>(&raw);
+    for (int j0 = 0; j0 < k; j0 += SB) {
+      float w[SB];
+      int p[SB];
 #pragma unroll
-        for (int z = 0; z < VEC; ++z) acc[z] += w * f[z];
-      } else {
-        const uint16_t *h = reinterpret_cast<const uint16_t *>(&raw);
-#pragma unroll
-        for (int z = 0; z < VEC; ++z) acc[z] += w * bf2f(h[z]);
+      for (int b = 0; b < SB; ++b) {
+        const int jj = min(j0 + b, k - 1);
+        w[b] = ld_coh(P.wts + (size_t)t * k + jj);
+        p[b] = ld_coh(P.inv_perm + (size_t)t * k + jj);
       }
-    }
-    if (P.S) {
-      const uint4 raw = ld_coh16(Y + ((size_t)P.T * P.k + t) * P.d + v * VEC);
-      if constexpr (WT == WF32) {
-        const float *f = reinterpret_cast<const float *>(&raw);
+      uint4 raw[SB];
 #pragma unroll
-        for (int z = 0; z < VEC; ++z) acc[z] += f[z];
-      } else {
-        const uint16_t *h = reinterpret_cast<const uint16_t *>(&raw);
+      for (int b = 0; b < SB; ++b) raw[b] = ld_coh16(Y + (size_t)min(max(p[b], 0), P.T * k - 1) * P.d + v * VEC);
 #pragma unroll
-        for (int z = 0; z < VEC; ++z) acc[z] += bf2f(h[z]);
-      }
+      for (int b = 0; b < SB; ++b)
+        if (j0 + b < k) add(acc, raw[b], w[b]);
     }
+    if (P.S) add(acc, ld_coh16(Y + ((size_t)P.T * k + t) * P.d + v * VEC), 1.0f);
     uint4 o;
     if constexpr (WT == WF32) {
       o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3]));

@@ -80,6 +80,7 @@ struct KParams {
   int phases;
   int bm, tk, gu_cols, dn_cols;
   int n_lt, n_le, n_kt, n_kc, n_shmt, nt_gu, nt_dn, n_comb, mt_cap;
+  int ctok;       // tokens per combine item
   int n_Z, n_L, n_K, n_SG, n_S;   // items per static phase (ticket order Z, L, K, SG, S)
   int gd_words, hist_words;       // words cleared by the Z items
   int schedule;  // 0 dynamic, 1 static
@@ -96,6 +97,8 @@ struct KParams {
   int *counts, *offsets, *perm, *inv_perm;
   int *ctrl, *gudone, *hist, *mtoff;
   int *mtok;      // 16-row m-tiles: token of each row, m-tile-major (rows past the end: stale)
+  int *dndone;    // per m-tile (shared first): down items done
+  int *slotmt;    // [T*k] routed m-tile of each (token, slot)
   int4 *desc;
   void *H, *Y;
   unsigned long long *trace;
@@ -781,8 +784,9 @@ __device__ __forceinline__ void chunk_masks(const KParams &P, int ntok, SM &sm) 
 // stable scatter of a chunk: slot (t, j) with expert e goes to
 //   offsets[e] + base[e] + #(earlier tokens of the chunk that chose e)
 // (a token chooses an expert at most once, so the rank is a popcount of the mask).
-// mto (16-row m-tiles): per-expert m-tile offsets; the slot's token is also written to the
-// m-tile token table (row r of expert e's rows: m-tile mto[e] + r / 16, row r % 16)
+// mto: per-expert m-tile offsets; the slot's m-tile (row r of expert e's rows is in m-tile
+// mto[e] + r / bm) goes to slotmt, and with 16-row m-tiles the slot's token also goes to the
+// m-tile token table
 template <class SM>
 __device__ __forceinline__ void chunk_scatter(const KParams &P, int c, int ntok, const int *offs, const int *base,
                                               const int *mto, SM &sm) {
@@ -802,7 +806,11 @@ __device__ __forceinline__ void chunk_scatter(const KParams &P, int c, int ntok,
     const int slot = t0 * k + q;
     st_coh(P.perm + p, slot);
     st_coh(P.inv_perm + slot, p);
-    if (mto) st_coh(P.mtok + (mto[e] + (r >> 4)) * 16 + (r & 15), t0 + tt);
+    if (P.phases & PH_FFN) {
+      const int gm = mto[e] + r / P.bm;
+      st_coh(P.slotmt + slot, gm);
+      if (P.bm == 16) st_coh(P.mtok + gm * 16 + (r & 15), t0 + tt);
+    }
   }
 }
 
@@ -954,7 +962,7 @@ __device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
   if (P.n_kt == 1) {
     plan_wg(P, sm, true);
     __syncthreads();
-    chunk_scatter(P, 0, ntok, sm.u.r.scan0, nullptr, P.bm == 16 ? sm.u.r.scan1 : nullptr, sm);
+    chunk_scatter(P, 0, ntok, sm.u.r.scan0, nullptr, sm.u.r.scan1, sm);
     wg_signal(P.ctrl + kSlotInts * C_KDONE);
     if (otid() == 0) __hip_atomic_fetch_add(P.ctrl + kSlotInts * C_PLAN, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
@@ -992,10 +1000,10 @@ __device__ __forceinline__ void scatter_item(const KParams &P, int c, SM &sm) {
   for (int e = tid; e < E; e += kThreads) {
     sm.u.r.scan0[e] = ld_coh(P.offsets + e);
     sm.u.r.scan1[e] = ld_coh(P.hist + (size_t)c * E + e);
-    if (P.bm == 16) sm.u.r.tmp[e] = ld_coh(P.mtoff + e);
+    if (P.phases & PH_FFN) sm.u.r.tmp[e] = ld_coh(P.mtoff + e);
   }
   __syncthreads();
-  chunk_scatter(P, c, ntok, sm.u.r.scan0, sm.u.r.scan1, P.bm == 16 ? sm.u.r.tmp : nullptr, sm);
+  chunk_scatter(P, c, ntok, sm.u.r.scan0, sm.u.r.scan1, sm.u.r.tmp, sm);
 }
 
 template <int WT> struct ActT { using type = uint16_t; };
@@ -1142,7 +1150,7 @@ __device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm, const
       }
     }
   }
-  wg_signal(P.ctrl + kSlotInts * C_DDONE);
+  wg_signal(P.dndone + gm);
   return true;
 }
 
@@ -1356,20 +1364,42 @@ __device__ __forceinline__ bool down_unit(const KParams &P, int i, SM &sm, bool 
     store4<WT>(P.Y, (hrow0 + j) * (size_t)P.d + o0 + 4 * g, acc[0]);
     store4<WT>(P.Y, (hrow0 + j) * (size_t)P.d + o0 + 16 + 4 * g, acc[1]);
   }
-  wg_signal(P.ctrl + kSlotInts * C_DDONE);
+  wg_signal(P.dndone + gm);
   return true;
 }
 
+// Waits (all threads) until the down items of every m-tile holding a row of combine item c
+// (its tokens' k slots and the shared expert's row) are done.  False on timeout or fault.
+template <class SM>
+__device__ __forceinline__ bool combine_ready(const KParams &P, int c, SM &sm) {
+  const int tid = otid(), k = P.k;
+  const int t0 = c * P.ctok, ntok = min(P.ctok, P.T - t0), nsl = ntok * k;
+  int *err = P.ctrl + kSlotInts * C_ERR;
+  bool ok = true;
+  for (int q = tid; q < nsl + (P.S ? ntok : 0); q += kThreads) {
+    const int gm = q < nsl ? P.n_shmt + ld_coh(P.slotmt + (size_t)t0 * k + q) : (t0 + q - nsl) / P.bm;
+    const int *ctr = P.dndone + min(max(gm, 0), P.mt_cap - 1);
+    if (ld_relaxed(ctr) < P.nt_dn && !spin_geq(ctr, P.nt_dn, err)) ok = false;
+  }
+  if (tid == 0) sm.bcast[1] = 1;
+  __syncthreads();
+  if (!ok) sm.bcast[1] = 0;
+  __syncthreads();
+  return uni(sm.bcast[1]) != 0;
+}
+
 // combine: out[t] = sum_j w[t,j] * Y[inv_perm[t*k+j]] (+ Y[T*k + t]), float32, slot order.
-// It runs after the last down unit, so its latency is the layer's tail: the slots are taken
-// 8 at a time, with all of their weights and row indices loaded first, then all 8 rows of Y.
+// It ends the layer, so latency matters: each thread keeps kCombineUnroll (token, column)
+// pairs in flight, and takes the slots 8 at a time, with all of their weights and row
+// indices loaded before all 8 rows of Y.
 template <int WT>
 __device__ __forceinline__ void combine_item(const KParams &P, int c) {
   using A = typename ActT<WT>::type;
   constexpr int VEC = 16 / sizeof(A);
   constexpr int SB = 8;  // slots per batch
-  const int t0 = c * kCombineTokens, ntok = min(kCombineTokens, P.T - t0);
-  const int nv = P.d / VEC, k = P.k;
+  constexpr int UN = kCombineUnroll;
+  const int t0 = c * P.ctok, ntok = min(P.ctok, P.T - t0);
+  const int nv = P.d / VEC, k = P.k, npair = ntok * nv;
   const A *Y = reinterpret_cast<const A *>(P.Y);
   A *out = reinterpret_cast<A *>(P.out);
   auto add = [&](float (&acc)[VEC], const uint4 &raw, float w) {
@@ -1383,38 +1413,56 @@ __device__ __forceinline__ void combine_item(const KParams &P, int c) {
       for (int z = 0; z < VEC; ++z) acc[z] += w * bf2f(h[z]);
     }
   };
-  for (int q = otid(); q < ntok * nv; q += kThreads) {
-    const int t = t0 + q / nv, v = q % nv;
-    float acc[VEC];
+  for (int q0 = otid(); q0 < npair; q0 += UN * kThreads) {
+    int t[UN], v[UN];
+    float acc[UN][VEC];
 #pragma unroll
-    for (int z = 0; z < VEC; ++z) acc[z] = 0.f;
+    for (int x = 0; x < UN; ++x) {
+      const int q = min(q0 + x * kThreads, npair - 1);  // (clamped: repeats a valid pair)
+      t[x] = t0 + q / nv;
+      v[x] = q % nv;
+#pragma unroll
+      for (int z = 0; z < VEC; ++z) acc[x][z] = 0.f;
+    }
     for (int j0 = 0; j0 < k; j0 += SB) {
-      float w[SB];
-      int p[SB];
+      float w[UN][SB];
+      int p[UN][SB];
 #pragma unroll
-      for (int b = 0; b < SB; ++b) {
-        const int jj = min(j0 + b, k - 1);
-        w[b] = ld_coh(P.wts + (size_t)t * k + jj);
-        p[b] = ld_coh(P.inv_perm + (size_t)t * k + jj);
+      for (int x = 0; x < UN; ++x)
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+          const size_t at = (size_t)t[x] * k + min(j0 + b, k - 1);
+          w[x][b] = ld_coh(P.wts + at);
+          p[x][b] = ld_coh(P.inv_perm + at);
+        }
+      uint4 raw[UN][SB];
+#pragma unroll
+      for (int x = 0; x < UN; ++x)
+#pragma unroll
+        for (int b = 0; b < SB; ++b)
+          raw[x][b] = ld_coh16(Y + (size_t)min(max(p[x][b], 0), P.T * k - 1) * P.d + v[x] * VEC);
+#pragma unroll
+      for (int x = 0; x < UN; ++x)
+#pragma unroll
+        for (int b = 0; b < SB; ++b)
+          if (j0 + b < k) add(acc[x], raw[x][b], w[x][b]);
+    }
+#pragma unroll
+    for (int x = 0; x < UN; ++x) {
+      if (q0 + x * kThreads >= npair) continue;
+      if (P.S) add(acc[x], ld_coh16(Y + ((size_t)P.T * k + t[x]) * P.d + v[x] * VEC), 1.0f);
+      uint4 o;
+      if constexpr (WT == WF32) {
+        o = make_uint4(__float_as_uint(acc[x][0]), __float_as_uint(acc[x][1]), __float_as_uint(acc[x][2]),
+                       __float_as_uint(acc[x][3]));
+      } else {
+        uint32_t wv[4];
+#pragma unroll
+        for (int z = 0; z < 4; ++z) wv[z] = (uint32_t)f2bf(acc[x][2 * z]) | ((uint32_t)f2bf(acc[x][2 * z + 1]) << 16);
+        o = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
-      uint4 raw[SB];
-#pragma unroll
-      for (int b = 0; b < SB; ++b) raw[b] = ld_coh16(Y + (size_t)min(max(p[b], 0), P.T * k - 1) * P.d + v * VEC);
-#pragma unroll
-      for (int b = 0; b < SB; ++b)
-        if (j0 + b < k) add(acc, raw[b], w[b]);
+      *reinterpret_cast<uint4 *>(out + (size_t)t[x] * P.d + v[x] * VEC) = o;
     }
-    if (P.S) add(acc, ld_coh16(Y + ((size_t)P.T * k + t) * P.d + v * VEC), 1.0f);
-    uint4 o;
-    if constexpr (WT == WF32) {
-      o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3]));
-    } else {
-      uint32_t wv[4];
-#pragma unroll
-      for (int z = 0; z < 4; ++z) wv[z] = (uint32_t)f2bf(acc[2 * z]) | ((uint32_t)f2bf(acc[2 * z + 1]) << 16);
-      o = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-    }
-    *reinterpret_cast<uint4 *>(out + (size_t)t * P.d + v * VEC) = o;
   }
 }
 
@@ -1446,7 +1494,7 @@ void moe_persistent(KParams P) {
   }
   const int n_Z = P.n_Z, n_L = P.n_L, n_K = P.n_K, n_SG = P.n_SG, n_S = P.n_S;
   const bool dyn = (P.phases & (PH_FFN | PH_COMBINE)) != 0;
-  bool zero_seen = false, logits_seen = false, plan_seen = false, scat_seen = false, dn_seen = false;
+  bool zero_seen = false, logits_seen = false, plan_seen = false, scat_seen = false;
   int n_mt = -1;
   int step = 0;
   const bool dynamic = P.schedule == 0;
@@ -1549,10 +1597,17 @@ void moe_persistent(KParams P) {
           kind = K_DN;
         }
       } else if ((i -= n_G + n_D) < P.n_comb) {
-        if (!dn_seen) {
-          if (!wg_wait(ctrl + kSlotInts * C_DDONE, n_D, err, sm)) break;
-          dn_seen = true;
+        // the token's rows of Y are final once the down items of their m-tiles are done (the
+        // slot m-tiles come from the scatter; the counters are valid once cleared)
+        if (!scat_seen) {
+          if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S, err, sm)) break;
+          scat_seen = true;
         }
+        if (!zero_seen) {
+          if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
+          zero_seen = true;
+        }
+        if (!combine_ready(P, i, sm)) break;
         combine_item<WT>(P, i);
         kind = K_COMB;
       } else {
@@ -1704,6 +1759,7 @@ moe_status launch(const Call &c) {
   P.nt_gu = L.nt_gu;
   P.nt_dn = L.nt_dn;
   P.n_comb = L.n_comb;
+  P.ctok = L.tiles.ctok;
   P.mt_cap = L.mt_routed_max + L.n_shmt;
   P.x = c.hidden;
   P.wr = c.w_router;
@@ -1732,6 +1788,8 @@ moe_status launch(const Call &c) {
   P.inv_perm = c.invperm_user ? c.invperm_user : reinterpret_cast<int *>(ws + L.off_invperm);
   P.ctrl = reinterpret_cast<int *>(ws);
   P.gudone = reinterpret_cast<int *>(ws + L.off_gudone);
+  P.dndone = P.gudone + ctr_words(L);
+  P.slotmt = reinterpret_cast<int *>(ws + L.off_slotmt);
   P.desc = reinterpret_cast<int4 *>(ws + L.off_desc);
   P.hist = reinterpret_cast<int *>(ws + L.off_hist);
   P.mtoff = reinterpret_cast<int *>(ws + L.off_mtoff);

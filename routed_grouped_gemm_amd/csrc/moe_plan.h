@@ -27,7 +27,7 @@ constexpr int kMaxK = 256;
 constexpr int kTopkTokens = 16;        // tokens per top-k item (4 per wave)
 constexpr int kMaxChunkTokens = 128;   // tokens per scatter chunk (rank bitmasks: 4 words)
 constexpr int kMaxChunkSlots = 1024;   // (token, slot) pairs per chunk
-constexpr int kCombineTokens = 1;      // combine item: 1 token
+constexpr int kCombineUnroll = 2;      // combine: (token, column) pairs per thread in flight
 constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroing item
 
 
@@ -51,6 +51,7 @@ struct Tiles {
   int gu_cols;     // H columns per gate/up item: 4 waves x nf/2 x 16 (16 when mg == 1)
   int dn_cols;     // output columns per down item: 4 waves x nf x 16 (128 when mg == 1)
   int tk;          // tokens per scatter chunk (tk <= 128, tk * k <= 1024)
+  int ctok;        // tokens per combine item (1 for small T: more items in parallel)
   int rt_tokens;   // router item: tokens x experts (16 x 16 split over the 4 waves when
   int rt_experts;  //   mg == 1, else 16 x 128 on the 16-row expert tile core)
 };
@@ -69,7 +70,7 @@ struct Layout {
   int64_t rows_h;        // rows of H and Y: T*k + n_shared*T
   // byte offsets into the workspace
   size_t off_gudone, off_desc, off_logits, off_ids, off_wts, off_hist, off_counts, off_offsets, off_mtoff,
-      off_perm, off_invperm, off_mtok, off_h, off_y, total;
+      off_perm, off_invperm, off_mtok, off_slotmt, off_h, off_y, total;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -115,12 +116,16 @@ inline Tiles choose_tiles(const moe_problem *p) {
   t.tk = kMaxChunkSlots / p->k;
   if (t.tk > kMaxChunkTokens) t.tk = kMaxChunkTokens;
   if (t.tk < 1) t.tk = 1;
+  t.ctok = p->T > 1024 ? 4 : 1;
   t.rt_tokens = 16;
   t.rt_experts = t.mg == 1 ? 16 : 128;
   return t;
 }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// words of one per-m-tile counter array (gate/up done, down done), padded to 256 bytes
+inline int ctr_words(const Layout &L) { return (int)align_up((size_t)(L.mt_routed_max + L.n_shmt + 1), 64); }
 
 // Work items of one launch, per phase, in ticket order: Z (clear counters), L (router),
 // K (top-k), SG (shared gate/up), S (scatter); the routed gate/up, down and combine items
@@ -147,7 +152,7 @@ inline Layout make_layout(const moe_problem *p) {
   L.n_shmt = p->n_shared ? (int)ceil_div(T, bm) : 0;
   L.nt_gu = p->n / L.tiles.gu_cols;
   L.nt_dn = (int)ceil_div(p->d, L.tiles.dn_cols);
-  L.n_comb = (int)ceil_div(T, kCombineTokens);
+  L.n_comb = (int)ceil_div(T, L.tiles.ctok);
   L.rows_h = tk + (int64_t)p->n_shared * T;
   const size_t asz = dtype_size(p->act_dtype);
   size_t o = kCtrlBytes;
@@ -156,7 +161,10 @@ inline Layout make_layout(const moe_problem *p) {
     o = align_up(o + bytes, 256);
     return at;
   };
-  L.off_gudone = take(sizeof(int32_t) * (size_t)(L.mt_routed_max + L.n_shmt + 1));
+  // per m-tile counters: gate/up items done, then (from word ctr_words) down items done; the
+  // two arrays start on separate 256-byte lines, so the down items' atomics never share a
+  // line with the gate/up counters that down units poll
+  L.off_gudone = take(sizeof(int32_t) * 2 * (size_t)ctr_words(L));
   L.off_desc = take(4 * sizeof(int32_t) * (size_t)(L.mt_routed_max + 1));
   L.off_logits = take(sizeof(float) * (size_t)(T * E));
   L.off_ids = take(sizeof(int32_t) * (size_t)tk);
@@ -168,6 +176,7 @@ inline Layout make_layout(const moe_problem *p) {
   L.off_perm = take(sizeof(int32_t) * (size_t)tk);
   L.off_invperm = take(sizeof(int32_t) * (size_t)tk);
   L.off_mtok = take(sizeof(int32_t) * (bm == 16 ? (size_t)L.mt_routed_max * 16 : 16));
+  L.off_slotmt = take(sizeof(int32_t) * (size_t)tk);
   L.off_h = take(asz * (size_t)L.rows_h * (size_t)p->n);
   L.off_y = take(asz * (size_t)L.rows_h * (size_t)p->d);
   L.total = o;
@@ -178,7 +187,7 @@ inline PhaseCounts phase_counts(const Layout &L, int phases) {
   PhaseCounts c{};
   const bool ffn = (phases & PH_FFN) != 0, perm = (phases & PH_PERMUTE) != 0;
   const bool many = L.n_kt > 1;  // one top-k item plans and scatters by itself
-  c.gd_words = ffn ? L.mt_routed_max + L.n_shmt : 0;
+  c.gd_words = ffn ? 2 * ctr_words(L) : 0;
   c.hist_words = (perm && many) ? L.n_kc * L.E : 0;
   c.z = (int)ceil_div(c.gd_words + c.hist_words, kZeroPerItem);
   c.l = (phases & PH_ROUTE) ? L.n_lt * L.n_le : 0;

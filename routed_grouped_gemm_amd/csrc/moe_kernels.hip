@@ -1499,15 +1499,18 @@ void moe_persistent(KParams P) {
   int step = 0;
   const bool dynamic = P.schedule == 0;
   // Dynamic tickets come from np = min(kTicketParts, grid) counters, one per partition of
-  // the workgroups (blockIdx % np): partition p hands out the tickets p, p + np, ... in
-  // order (every partition has a workgroup, so every ticket has a taker).  Device atomics on one address serialise (~11 ns each), and every workgroup takes
+  // the workgroups: partition p hands out the tickets p, p + np, ... in order.  Workgroup b
+  // joins partition (b + b / 8) % np: the hardware deals workgroups to the 8 XCDs round
+  // robin (b % 8), so every partition draws on all XCDs, and a partition that falls behind
+  // near the end still has the whole chip's bandwidth; workgroup b < np joins partition b,
+  // so every partition has a workgroup and every ticket a taker.  Device atomics on one address serialise (~11 ns each), and every workgroup takes
   // a ticket at start-up and one per item: split over the partitions, neither the start-up
   // burst nor the steady stream of ticket atomics queues up behind one address.  A ticket is
   // still only ever taken by a running workgroup, and each partition's workgroups take their
   // tickets in increasing order while waiting only for smaller tickets, so every wait ends
   // (induction over the tickets, as with one counter).  Thread 0 keeps the next ticket
   // prefetched, so the atomic's latency overlaps the current item.
-  const int nparts = min(kTicketParts, (int)gridDim.x), part = (int)blockIdx.x % nparts;
+  const int nparts = min(kTicketParts, (int)gridDim.x), part = ((int)blockIdx.x + (int)blockIdx.x / 8) % nparts;
   int *pctr = ctrl + kSlotInts * (C_PTICKET + part);
   int next = 0;
   if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1626,14 +1629,18 @@ void moe_persistent(KParams P) {
       rec[3] = ((unsigned long long)blockIdx.x << 32) | (unsigned)kind;
     }
   }
-  // the last workgroup out resets the control block for the next call
+  // The last workgroup out resets the control block for the next call.  Thread 0 made every
+  // counter update of this workgroup (the unused prefetched ticket included); once they have
+  // all returned, a relaxed increment of the exit counter orders them before the reset.  No
+  // acquire or release here: at agent scope those write back and invalidate the XCD's whole
+  // L2, and with every workgroup leaving at the end that would stall the items still running.
   __syncthreads();
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(ctrl + kSlotInts * C_EXIT, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    wait_vm0();
+    const int old = __hip_atomic_fetch_add(ctrl + kSlotInts * C_EXIT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (int)gridDim.x - 1) {
-      for (int s = C_TICKET; s <= C_NMT; ++s) ctrl[kSlotInts * s] = 0;
-      for (int q = 0; q < kTicketParts; ++q) ctrl[kSlotInts * (C_PTICKET + q)] = 0;
-      __threadfence();
+      for (int s = C_TICKET; s <= C_NMT; ++s) st_coh(ctrl + kSlotInts * s, 0);
+      for (int q = 0; q < kTicketParts; ++q) st_coh(ctrl + kSlotInts * (C_PTICKET + q), 0);
     }
   }
 }

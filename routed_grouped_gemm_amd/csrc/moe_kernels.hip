@@ -98,6 +98,8 @@ struct KParams {
   int *ctrl, *gudone, *hist, *mtoff;
   int *mtok;      // 16-row m-tiles: token of each row, m-tile-major (rows past the end: stale)
   int *dndone;    // per m-tile (shared first): down items done
+  int rt_split;   // K splits per router tile; > 1: partial logits in lpart [rt_split][T][E]
+  float *lpart;
   int *slotmt;    // [T*k] routed m-tile of each (token, slot)
   int4 *desc;
   void *H, *Y;
@@ -245,21 +247,25 @@ constexpr uint64_t kSpinTicks = 200000000ull;  // ~2 s of the 100 MHz wall clock
 // poll); the caller issues one acquire fence after the wait succeeds.  Polls back off
 // from ~0.1 us to ~0.9 us apart: hundreds of waiting workgroups polling one address at full
 // rate would saturate that address's memory channel and slow every other load.
-__device__ __forceinline__ bool spin_geq(const int *p, int target, int *err) {
-  if (ld_relaxed(p) >= target) return true;
+// spin_value returns the value it saw (>= target >= 0), or -1 on timeout or fault.
+__device__ __forceinline__ int spin_value(const int *p, int target, int *err) {
+  int v = ld_relaxed(p);
+  if (v >= target) return v;
   const uint64_t t0 = wall_clock64();
   for (int it = 0;; ++it) {
     if (it < 8) __builtin_amdgcn_s_sleep(4);
     else if (it < 32) __builtin_amdgcn_s_sleep(12);
     else __builtin_amdgcn_s_sleep(32);
-    if (ld_relaxed(p) >= target) return true;
-    if (ld_relaxed(err) != 0) return false;
+    v = ld_relaxed(p);
+    if (v >= target) return v;
+    if (ld_relaxed(err) != 0) return -1;
     if (wall_clock64() - t0 > kSpinTicks) {
       __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
+      return -1;
     }
   }
 }
+__device__ __forceinline__ bool spin_geq(const int *p, int target, int *err) { return spin_value(p, target, err) >= 0; }
 
 __device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
   // exact for values with <= 8 significant bits (decoded fp8 values)
@@ -556,6 +562,30 @@ __device__ __forceinline__ bool wg_wait(const int *p, int target, int *err, SM &
   return uni(sm.bcast[1]) != 0;
 }
 
+// Publishes the plan: n_mt + 1 goes into every copy of the plan flag once this workgroup's
+// plan (and scatter) stores have completed.  Most of the grid waits for the plan at the
+// start of the layer; polls of one word would all queue at one memory channel and hold up
+// every other access to it (the routing's own loads among them), so each workgroup polls
+// a copy of its own.
+__device__ __forceinline__ void plan_publish(const KParams &P, int nmt) {
+  wait_vm0();
+  __syncthreads();
+  const int tid = otid();
+  if (tid < kPlanCopies) st_coh(P.ctrl + plan_flag_word(tid), nmt + 1);
+}
+
+// Waits for the plan (this workgroup's copy of the flag); returns n_mt, or -1 on timeout.
+template <class SM>
+__device__ __forceinline__ int wg_wait_plan(const KParams &P, SM &sm) {
+  __syncthreads();
+  if (otid() == 0) {
+    const int v = spin_value(P.ctrl + plan_flag_word((int)blockIdx.x % kPlanCopies), 1, P.ctrl + kSlotInts * C_ERR);
+    sm.bcast[1] = v < 0 ? -1 : v - 1;
+  }
+  __syncthreads();
+  return uni(sm.bcast[1]);
+}
+
 // ---------------------------------------------------------------------------------
 // phase items
 // ---------------------------------------------------------------------------------
@@ -568,32 +598,52 @@ __device__ __forceinline__ void zero_item(const KParams &P, int i) {
   }
 }
 
-// router logits, decode-sized tiles: 16 tokens x 16 experts; wave w sums the K range
-// [w*d/4, (w+1)*d/4), then the four partial sums are added in wave order.  Latency matters
-// here (the rest of the layer waits for the routing), so each wave issues all of its loads
-// of a 16-step chunk (and the bias) before the first MFMA: one memory round trip per chunk.
-// Steps past the end read the last step again and multiply zero activations.
+// router logits, decode-sized tiles: 16 tokens x 16 experts over part ks of S = rt_split
+// equal parts of K; wave w sums the w-th quarter of that part, then the four partial sums
+// are added in wave order.  With S == 1 the item adds the bias and writes the logits; else
+// it writes its partial sums to lpart[ks], and the top-k items add the S parts in order.
+// Latency matters here (the rest of the layer waits for the routing), so each wave issues
+// all of its loads of a 16-step chunk (and the bias) before the first MFMA: one memory
+// round trip per chunk.  Steps past the end read the last step again and multiply zero
+// activations.
 template <int WT, class SM>
 __device__ __forceinline__ void logits_item_split(const KParams &P, int i, SM &sm) {
   constexpr int RT = (WT == WF32) ? WF32 : WBF16;  // the router runs in the activation dtype
   constexpr int KU = Ty<RT>::KU, ASZ = Ty<RT>::ASZ;
   constexpr int CH = 16;  // K steps per chunk
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
-  const int lt = i / P.n_le, le = i % P.n_le;
+  const int S = P.rt_split, ls = S == 4 ? 2 : S == 2 ? 1 : 0;  // (S is 1, 2 or 4: shifts)
+  const int ks = i & (S - 1), tile = i >> ls;
+  const int lt = tile / P.n_le, le = tile % P.n_le;
   const int t0 = lt * 16, e0 = le * 16;
-  const int kq = P.d / kWaves, kbeg = wv * kq;
+  const int kq = P.d >> (2 + ls), kbeg = ks * (P.d >> ls) + wv * kq;
   const int er = min(e0 + j, P.E - 1), tr = min(t0 + j, P.T - 1);
   const char *wp = reinterpret_cast<const char *>(P.wr) + ((size_t)er * P.d + kbeg) * ASZ + g * 16;
   const char *xp = reinterpret_cast<const char *>(P.x) + ((size_t)tr * P.d + kbeg) * ASZ + g * 16;
   float bias[4] = {0.f, 0.f, 0.f, 0.f};
-  if (P.bias) {
+  if (P.bias && S == 1) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) bias[r] = P.bias[min(e0 + 4 * g + r, P.E - 1)];
   }
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
   const int nsteps = kq / KU;
   const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-  for (int s0 = 0; s0 < nsteps; s0 += CH) {
+  int s0 = 0;
+  // full chunks: one base address each, the steps at immediate offsets (short code, which
+  // matters here: the item runs once per layer, so its instructions are fetched cold)
+  for (; s0 + CH <= nsteps; s0 += CH) {
+    uint4 w[CH], a[CH];
+    const char *wc = wp + (size_t)s0 * 64, *xc = xp + (size_t)s0 * 64;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      w[u] = ld_glob16(wc + u * 64);
+      a[u] = ld_glob16(xc + u * 64);
+    }
+    asm volatile("" ::: "memory");  // every load of the chunk is in flight before the first MFMA
+#pragma unroll
+    for (int u = 0; u < CH; ++u) acc = mfma_step<RT>(w[u], a[u], a[u], acc);
+  }
+  if (s0 < nsteps) {  // last, partial chunk
     uint4 w[CH], a[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
@@ -601,7 +651,7 @@ __device__ __forceinline__ void logits_item_split(const KParams &P, int i, SM &s
       w[u] = ld_glob16(wp + off);
       a[u] = ld_glob16(xp + off);
     }
-    asm volatile("" ::: "memory");  // every load of the chunk is in flight before the first MFMA
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const uint4 av = s0 + u < nsteps ? a[u] : z4;
@@ -619,7 +669,9 @@ __device__ __forceinline__ void logits_item_split(const KParams &P, int i, SM &s
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int e = e0 + 4 * g + r;
-        if (e < P.E) st_coh(P.logits + (size_t)t * P.E + e, sum[r] + bias[r]);
+        if (e >= P.E) continue;
+        if (S == 1) st_coh(P.logits + (size_t)t * P.E + e, sum[r] + bias[r]);
+        else st_coh(P.lpart + ((size_t)ks * P.T + t) * P.E + e, sum[r]);
       }
     }
   }
@@ -814,6 +866,42 @@ __device__ __forceinline__ void chunk_scatter(const KParams &P, int c, int ntok,
   }
 }
 
+// gate weights of TPW selected tokens: the softmax of the kept logits, summed in slot order.
+// k <= 64: slot j's logit and id are in lane j; k > 64: the ids are in LDS and the logits
+// are read again from memory (the same values, -0.0 read as +0.0).
+template <int TPW>
+__device__ __forceinline__ void topk_weights(const KParams &P, const int (&t)[TPW], const bool (&live)[TPW],
+                                             const float (&lj)[TPW], const int (&ej)[TPW],
+                                             int16_t *const (&ids_lds)[TPW]) {
+  const int lane = otid() & 63, k = P.k, E = P.E;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    if (!live[u]) continue;
+    if (k <= 64) {
+      const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj[u]), 0));
+      const float z = lane < k ? expf(lj[u] - l0) : 0.f;
+      float ssum = 0.f;
+      for (int jj = 0; jj < k; ++jj) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), jj));
+      if (lane < k) {
+        st_coh(P.wts + (size_t)t[u] * k + lane, z / ssum);
+        st_coh(P.ids + (size_t)t[u] * k + lane, ej[u]);
+      }
+    } else {
+      if (P.rt_split > 1) wait_vm0();  // this wave's own logits stores (split router)
+      if (lane != 0) continue;
+      const float *Lr = P.logits + (size_t)t[u] * E;
+      const float l0 = ld_coh(Lr + ids_lds[u][0]) + 0.0f;
+      float ssum = 0.f;
+      for (int jj = 0; jj < k; ++jj) ssum += expf((ld_coh(Lr + ids_lds[u][jj]) + 0.0f) - l0);
+      for (int jj = 0; jj < k; ++jj) {
+        const int e = ids_lds[u][jj];
+        st_coh(P.wts + (size_t)t[u] * k + jj, expf((ld_coh(Lr + e) + 0.0f) - l0) / ssum);
+        st_coh(P.ids + (size_t)t[u] * k + jj, e);
+      }
+    }
+  }
+}
+
 // top-k of TPW tokens on one wave, in lockstep (their reductions are independent, so they
 // overlap).  Lane l holds the keys of experts l, l + 64, ... (NQ of them): the ordered
 // 32-bit image of the logit, 0 for absent or already taken experts.  Each round takes the
@@ -865,31 +953,103 @@ __device__ __forceinline__ void topk_group(const KParams &P, const int (&t)[TPW]
       if (lane == 0 && live[u]) ids_lds[u][jj] = (int16_t)c[u];
     }
   }
+  topk_weights<TPW>(P, t, live, lj, ej, ids_lds);
+}
+
+// Selection of the same order for E <= 256 (4 keys per lane), with about half the work per
+// round.  Each lane first sorts its 4 keys, largest first; the adjacent compare-exchanges
+// swap only on a strictly larger key, so equal keys keep their increasing expert ids.  A
+// round then needs one wave max over the lanes' heads: the lanes whose head equals it are
+// a ballot, and when only one lane holds the maximum (the usual case) its head is the
+// winner.  Several tied lanes take the lowest id among their heads (wave max of the
+// complemented ids).  The winning lane drops its head.  Slot j's id and logit land in
+// lane j (k <= 64); for k > 64 lane 0 also writes the ids to LDS.
+template <int TPW>
+__device__ __forceinline__ void topk_group4(const KParams &P, const int (&t)[TPW], const bool (&live)[TPW],
+                                            uint32_t (&key)[TPW][4], int16_t *const (&ids_lds)[TPW]) {
+  const int lane = otid() & 63, k = P.k;
+  int qq[TPW][4];
+  float lj[TPW];
+  int ej[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    if (!live[u]) continue;
-    if (k <= 64) {
-      const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj[u]), 0));
-      const float z = lane < k ? expf(lj[u] - l0) : 0.f;
-      float ssum = 0.f;
-      for (int jj = 0; jj < k; ++jj) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), jj));
-      if (lane < k) {
-        st_coh(P.wts + (size_t)t[u] * k + lane, z / ssum);
-        st_coh(P.ids + (size_t)t[u] * k + lane, ej[u]);
-      }
-    } else if (lane == 0) {
-      // k > 64: the kept logits again from memory (the same values, -0.0 read as +0.0)
-      const float *Lr = P.logits + (size_t)t[u] * E;
-      const float l0 = ld_coh(Lr + ids_lds[u][0]) + 0.0f;
-      float ssum = 0.f;
-      for (int jj = 0; jj < k; ++jj) ssum += expf((ld_coh(Lr + ids_lds[u][jj]) + 0.0f) - l0);
-      for (int jj = 0; jj < k; ++jj) {
-        const int e = ids_lds[u][jj];
-        st_coh(P.wts + (size_t)t[u] * k + jj, expf((ld_coh(Lr + e) + 0.0f) - l0) / ssum);
-        st_coh(P.ids + (size_t)t[u] * k + jj, e);
+    lj[u] = 0.f;
+    ej[u] = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) qq[u][q] = q;
+  }
+  auto cx = [&](int u, int a, int b) {
+    const bool sw = key[u][b] > key[u][a];
+    const uint32_t ka = key[u][a], kb = key[u][b];
+    const int qa = qq[u][a], qb = qq[u][b];
+    key[u][a] = sw ? kb : ka;
+    key[u][b] = sw ? ka : kb;
+    qq[u][a] = sw ? qb : qa;
+    qq[u][b] = sw ? qa : qb;
+  };
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {  // odd-even transposition sort: 4 rounds for 4 keys
+    cx(u, 0, 1);
+    cx(u, 2, 3);
+    cx(u, 1, 2);
+    cx(u, 0, 1);
+    cx(u, 2, 3);
+    cx(u, 1, 2);
+  }
+  for (int jj = 0; jj < k; ++jj) {
+    uint32_t m[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) m[u] = key[u][0];
+    wave_max_u32<TPW>(m);
+    uint64_t tie[TPW];
+    bool many = false;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      tie[u] = __builtin_amdgcn_ballot_w64(key[u][0] == m[u]);
+      many |= __builtin_popcountll(tie[u]) > 1;
+    }
+    int win[TPW];
+    if (many) {
+      uint32_t c[TPW];
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) c[u] = key[u][0] == m[u] ? ~(uint32_t)(qq[u][0] * 64 + lane) : 0u;
+      wave_max_u32<TPW>(c);
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) win[u] = (int)~c[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int wl = (int)__builtin_ctzll(tie[u]);
+        win[u] = __builtin_amdgcn_readlane(qq[u][0], wl) * 64 + wl;
       }
     }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const bool pop = lane == (win[u] & 63);
+      key[u][0] = pop ? key[u][1] : key[u][0];
+      key[u][1] = pop ? key[u][2] : key[u][1];
+      key[u][2] = pop ? key[u][3] : key[u][2];
+      key[u][3] = pop ? 0u : key[u][3];
+      qq[u][0] = pop ? qq[u][1] : qq[u][0];
+      qq[u][1] = pop ? qq[u][2] : qq[u][1];
+      qq[u][2] = pop ? qq[u][3] : qq[u][2];
+      if (lane == (jj & 63)) {
+        lj[u] = key_value(m[u]);
+        ej[u] = win[u];
+      }
+    }
+    if (k > 64) {
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+        if (lane == 0 && live[u]) ids_lds[u][jj] = (int16_t)win[u];
+    }
   }
+  if (k <= 64) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+      if (live[u] && lane < k) ids_lds[u][lane] = (int16_t)ej[u];
+  }
+  topk_weights<TPW>(P, t, live, lj, ej, ids_lds);
 }
 
 // top-k + softmax for the kTopkTokens tokens of item c.  For E <= 256 a wave handles its 4
@@ -911,17 +1071,42 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
       live[u] = tt < ntok;
       t[u] = t0 + min(tt, ntok - 1);
       ids[u] = sm.u.r.ids + tt * k;
-      const float *Lr = P.logits + (size_t)t[u] * E;
+    }
+    // split router (rt_split > 1): lpart holds the K parts of the logits, added here in part
+    // order, then the bias; the finished logits are written out (the routing's logits
+    // output; the k > 64 path reads them back)
+    const int S = P.rt_split;
+    const float *L0 = S == 1 ? P.logits : P.lpart;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const float *Lr = L0 + (size_t)t[u] * E;
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[u][q] = ld_coh(Lr + min(q * 64 + lane, E - 1));
     }
     asm volatile("" ::: "memory");  // all of the wave's loads are in flight before any is used
+    if (S > 1) {
+      for (int ks = 1; ks < S; ++ks) {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[u][q] += ld_coh(P.lpart + ((size_t)ks * P.T + t[u]) * E + min(q * 64 + lane, E - 1));
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float bq = P.bias ? P.bias[min(q * 64 + lane, E - 1)] : 0.f;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          v[u][q] += bq;
+          if (live[u] && q * 64 + lane < E) st_coh(P.logits + (size_t)t[u] * E + q * 64 + lane, v[u][q]);
+        }
+      }
+    }
     uint32_t key[TPW][4];
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
 #pragma unroll
       for (int q = 0; q < 4; ++q) key[u][q] = (q * 64 + lane < E) ? ordered_key(v[u][q]) : 0u;
-    topk_group<4, TPW>(P, t, live, key, ids);
+    topk_group4<TPW>(P, t, live, key, ids);
   } else {
     for (int tt = wave; tt < ntok; tt += kWaves) {
       const int t[1] = {t0 + tt};
@@ -929,8 +1114,20 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
       int16_t *const ids[1] = {sm.u.r.ids + tt * k};
       const float *Lr = P.logits + (size_t)t[0] * E;
       float v[kMaxE / 64];
+      if (P.rt_split == 1) {
 #pragma unroll
-      for (int q = 0; q < kMaxE / 64; ++q) v[q] = ld_coh(Lr + min(q * 64 + lane, E - 1));
+        for (int q = 0; q < kMaxE / 64; ++q) v[q] = ld_coh(Lr + min(q * 64 + lane, E - 1));
+      } else {
+#pragma unroll
+        for (int q = 0; q < kMaxE / 64; ++q) {
+          const int e = min(q * 64 + lane, E - 1);
+          float x = ld_coh(P.lpart + (size_t)t[0] * E + e);
+          for (int ks = 1; ks < P.rt_split; ++ks) x += ld_coh(P.lpart + ((size_t)ks * P.T + t[0]) * E + e);
+          x += P.bias ? P.bias[e] : 0.f;
+          v[q] = x;
+          if (q * 64 + lane < E) st_coh(P.logits + (size_t)t[0] * E + e, x);
+        }
+      }
       uint32_t key[1][kMaxE / 64];
 #pragma unroll
       for (int q = 0; q < kMaxE / 64; ++q) key[0][q] = (q * 64 + lane < E) ? ordered_key(v[q]) : 0u;
@@ -963,8 +1160,7 @@ __device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
     plan_wg(P, sm, true);
     __syncthreads();
     chunk_scatter(P, 0, ntok, sm.u.r.scan0, nullptr, sm.u.r.scan1, sm);
-    wg_signal(P.ctrl + kSlotInts * C_KDONE);
-    if (otid() == 0) __hip_atomic_fetch_add(P.ctrl + kSlotInts * C_PLAN, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    plan_publish(P, sm.u.r.scan1[E]);
     return;
   }
   if (P.tk % kTopkTokens == 0) {  // the item lies in one chunk: add its histogram
@@ -985,7 +1181,7 @@ __device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
   __syncthreads();
   if (uni(sm.bcast[2])) {
     plan_wg(P, sm, false);
-    wg_signal(P.ctrl + kSlotInts * C_PLAN);
+    plan_publish(P, sm.u.r.scan1[E]);
   }
 }
 
@@ -1494,7 +1690,7 @@ void moe_persistent(KParams P) {
   }
   const int n_Z = P.n_Z, n_L = P.n_L, n_K = P.n_K, n_SG = P.n_SG, n_S = P.n_S;
   const bool dyn = (P.phases & (PH_FFN | PH_COMBINE)) != 0;
-  bool zero_seen = false, logits_seen = false, plan_seen = false, scat_seen = false;
+  bool zero_seen = false, logits_seen = false, scat_seen = false;
   int n_mt = -1;
   int step = 0;
   const bool dynamic = P.schedule == 0;
@@ -1557,21 +1753,14 @@ void moe_persistent(KParams P) {
       else gateup_item<WT, MG>(P, true, i, sm, lb);
       kind = K_SHGU;
     } else if ((i -= n_SG) < n_S) {
-      if (!plan_seen) {
-        if (!wg_wait(ctrl + kSlotInts * C_PLAN, 1, err, sm)) break;
-        plan_seen = true;
-      }
+      if (n_mt < 0 && (n_mt = wg_wait_plan(P, sm)) < 0) break;
       scatter_item(P, i, sm);
       wg_signal(ctrl + kSlotInts * C_SDONE);
       kind = K_SCATTER;
     } else {
       i -= n_S;
       if (!dyn) break;
-      if (!plan_seen) {
-        if (!wg_wait(ctrl + kSlotInts * C_PLAN, 1, err, sm)) break;
-        plan_seen = true;
-      }
-      if (n_mt < 0) n_mt = uni(ld_relaxed(ctrl + kSlotInts * C_NMT));
+      if (n_mt < 0 && (n_mt = wg_wait_plan(P, sm)) < 0) break;
       const int n_G = n_mt * P.nt_gu;
       const int n_D = (n_mt + P.n_shmt) * P.nt_dn;
       // small-tile units: a deep prefetch (8 steps) when the units are too few to keep the
@@ -1641,6 +1830,7 @@ void moe_persistent(KParams P) {
     if (old == (int)gridDim.x - 1) {
       for (int s = C_TICKET; s <= C_NMT; ++s) st_coh(ctrl + kSlotInts * s, 0);
       for (int q = 0; q < kTicketParts; ++q) st_coh(ctrl + kSlotInts * (C_PTICKET + q), 0);
+      for (int c = 0; c < kPlanCopies; ++c) st_coh(ctrl + plan_flag_word(c), 0);
     }
   }
 }
@@ -1760,6 +1950,7 @@ moe_status launch(const Call &c) {
   P.dn_cols = L.tiles.dn_cols;
   P.n_lt = L.n_lt;
   P.n_le = L.n_le;
+  P.rt_split = L.tiles.rt_split;
   P.n_kt = L.n_kt;
   P.n_kc = L.n_kc;
   P.n_shmt = L.n_shmt;
@@ -1787,6 +1978,7 @@ moe_status launch(const Call &c) {
   }
   P.out = c.out;
   P.logits = c.logits_user ? c.logits_user : reinterpret_cast<float *>(ws + L.off_logits);
+  P.lpart = reinterpret_cast<float *>(ws + L.off_lpart);
   P.ids = c.ids_user ? c.ids_user : (c.ids_in ? const_cast<int *>(c.ids_in) : reinterpret_cast<int *>(ws + L.off_ids));
   P.wts = c.wts_user ? c.wts_user : reinterpret_cast<float *>(ws + L.off_wts);
   P.counts = c.counts_user ? c.counts_user : reinterpret_cast<int *>(ws + L.off_counts);

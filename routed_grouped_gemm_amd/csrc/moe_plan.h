@@ -33,12 +33,16 @@ constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroin
 
 // control-block slots (one int32 each, at int index slot * kSlotInts): a poll of one
 // counter never shares a cache line or channel with the ticket counter or another counter.
-// C_PTICKET + p (p < kTicketParts): ticket counter of partition p (the workgroups with
-// blockIdx % kTicketParts == p), see the persistent kernel; C_TICKET is unused.
+// C_PTICKET + p (p < kTicketParts): ticket counter of partition p, see the persistent
+// kernel; C_TICKET and C_PLAN are unused.
 enum CtrlSlot : int {
   C_MAGIC = 0, C_TICKET = 1, C_ZDONE = 2, C_LDONE = 3, C_KDONE = 4, C_PLAN = 5, C_SDONE = 6,
-  C_DDONE = 7, C_EXIT = 8, C_NMT = 9, C_ERR = 10, C_PTICKET = 16, C_NSLOTS = kCtrlSlots
+  C_DDONE = 7, C_EXIT = 8, C_NMT = 9, C_ERR = 10, C_PTICKET = 16, C_PLANB = 24, C_NSLOTS = kCtrlSlots
 };
+// C_PLANB .. C_PLANB + 7: copies of the plan flag (n_mt + 1 once the plan is published),
+// eight per slot, 512 bytes apart; workgroup b polls copy b % kPlanCopies
+constexpr int kPlanCopies = 64;
+constexpr int plan_flag_word(int c) { return kSlotInts * (C_PLANB + (c >> 3)) + (c & 7) * 128; }
 constexpr int kMagic = 0x4d6f4531;     // "MoE1"
 
 // which phases a launch runs
@@ -54,6 +58,8 @@ struct Tiles {
   int ctok;        // tokens per combine item (1 for small T: more items in parallel)
   int rt_tokens;   // router item: tokens x experts (16 x 16 split over the 4 waves when
   int rt_experts;  //   mg == 1, else 16 x 128 on the 16-row expert tile core)
+  int rt_split;    // K splits per router tile (1, 2 or 4): with few tiles, each item takes
+                   //   one part of K and the top-k items add the partial sums in order
 };
 
 struct Layout {
@@ -69,7 +75,7 @@ struct Layout {
   int n_comb;            // combine items
   int64_t rows_h;        // rows of H and Y: T*k + n_shared*T
   // byte offsets into the workspace
-  size_t off_gudone, off_desc, off_logits, off_ids, off_wts, off_hist, off_counts, off_offsets, off_mtoff,
+  size_t off_gudone, off_desc, off_logits, off_lpart, off_ids, off_wts, off_hist, off_counts, off_offsets, off_mtoff,
       off_perm, off_invperm, off_mtok, off_slotmt, off_h, off_y, total;
 };
 
@@ -143,6 +149,13 @@ inline Layout make_layout(const moe_problem *p) {
   L.E = (int)E;
   L.n_lt = (int)ceil_div(T, L.tiles.rt_tokens);
   L.n_le = (int)ceil_div(E, L.tiles.rt_experts);
+  // a router item's waves each issue one chunk of loads (16 steps, 512 K) per memory round
+  // trip: with few tiles and a long K, K is split over 2 or 4 items per tile so that each
+  // wave needs one chunk (each wave's part of K stays a multiple of 32).  Short K is not
+  // split: the router items are the first of the launch, and more of them only start later.
+  L.tiles.rt_split = 1;
+  if (L.tiles.mg == 1 && (int64_t)L.n_lt * L.n_le < 64 && p->d > 2048)
+    L.tiles.rt_split = (p->d > 4096 && p->d % 512 == 0) ? 4 : 2;
   L.n_kt = (int)ceil_div(T, kTopkTokens);
   L.n_kc = (int)ceil_div(T, L.tiles.tk);
   const int64_t tk = T * k;
@@ -167,6 +180,7 @@ inline Layout make_layout(const moe_problem *p) {
   L.off_gudone = take(sizeof(int32_t) * 2 * (size_t)ctr_words(L));
   L.off_desc = take(4 * sizeof(int32_t) * (size_t)(L.mt_routed_max + 1));
   L.off_logits = take(sizeof(float) * (size_t)(T * E));
+  L.off_lpart = take(L.tiles.rt_split > 1 ? sizeof(float) * (size_t)L.tiles.rt_split * (size_t)(T * E) : 0);
   L.off_ids = take(sizeof(int32_t) * (size_t)tk);
   L.off_wts = take(sizeof(float) * (size_t)tk);
   L.off_hist = take(sizeof(int32_t) * (size_t)L.n_kc * (size_t)E);
@@ -190,7 +204,7 @@ inline PhaseCounts phase_counts(const Layout &L, int phases) {
   c.gd_words = ffn ? 2 * ctr_words(L) : 0;
   c.hist_words = (perm && many) ? L.n_kc * L.E : 0;
   c.z = (int)ceil_div(c.gd_words + c.hist_words, kZeroPerItem);
-  c.l = (phases & PH_ROUTE) ? L.n_lt * L.n_le : 0;
+  c.l = (phases & PH_ROUTE) ? L.n_lt * L.n_le * L.tiles.rt_split : 0;
   c.k = (phases & (PH_ROUTE | PH_PERMUTE)) ? L.n_kt : 0;
   c.sg = ffn ? L.n_shmt * L.nt_gu : 0;
   c.s = (perm && many) ? L.n_kc : 0;

@@ -53,6 +53,8 @@ ADHOC = [
     (17, 9, 256, 256, 1, 1, "bf16", "bf16", 0, False),     # E = 1, k = 1
     (18, 200, 1024, 512, 64, 6, "bf16", "fp8", 1, True),   # ~19 rows/expert -> 32-row tiles
     (19, 160, 512, 256, 8, 2, "bf16", "bf16", 0, False),   # ~40 rows/expert -> 64-row tiles
+    (20, 5, 4608, 256, 320, 4, "bf16", "bf16", 0, True),   # E > 256; router K in four parts
+    (21, 3, 2560, 256, 24, 3, "bf16", "bf16", 1, True),    # router K in two parts
 ]
 
 

@@ -81,7 +81,7 @@ struct KParams {
   int bm, tk, gu_cols, dn_cols;
   int n_lt, n_le, n_kt, n_kc, n_shmt, nt_gu, nt_dn, n_comb, mt_cap;
   int ctok;       // tokens per combine item
-  int n_Z, n_L, n_K, n_SG, n_S;   // items per static phase (ticket order Z, L, K, SG, S)
+  int n_Z, n_L, n_K, n_SG, n_S;   // items per static phase (order Z, L, K, SG, S)
   int gd_words, hist_words;       // words cleared by the Z items
   int schedule;  // 0 dynamic, 1 static
   const void *x, *wr;
@@ -1710,6 +1710,33 @@ void moe_persistent(KParams P) {
   int *pctr = ctrl + kSlotInts * (C_PTICKET + part);
   int next = 0;
   if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // item trace record (moe_forward_ex with a trace buffer); `item` numbers every item of the
+  // launch, router items included, in phase order
+  auto record = [&](int item, int kind, uint64_t t_start) {
+    if (P.trace && tid == 0 && item < P.trace_cap) {
+      unsigned long long *rec = P.trace + 4 * (size_t)item;
+      rec[0] = t_start;
+      rec[1] = wall_clock64();
+      // item | tile-loop start and end (16-bit offsets from the item start, 10 ns units)
+      const uint32_t m0 = sm.mark[0], m1 = sm.mark[1];
+      const unsigned long long d0 = m0 ? min((uint32_t)(m0 - (uint32_t)t_start), 0xffffu) : 0;
+      const unsigned long long d1 = m1 ? min((uint32_t)(m1 - (uint32_t)t_start), 0xffffu) : 0;
+      rec[2] = (unsigned long long)(uint32_t)item | (d0 << 32) | (d1 << 48);
+      rec[3] = ((unsigned long long)blockIdx.x << 32) | (unsigned)kind;
+    }
+  };
+  // Router items take no ticket: workgroup b runs items b, b + grid, ... before its first
+  // ticket.  They wait for nothing, so each finishes, and the first workgroups of the launch
+  // start on them at once rather than after a ticket atomic of the start-up burst.
+  for (int r = (int)blockIdx.x; r < n_L; r += (int)gridDim.x) {
+    __syncthreads();
+    const uint64_t t_start = P.trace ? wall_clock64() : 0;
+    if (P.trace && tid == 0) sm.mark[0] = sm.mark[1] = 0;
+    if constexpr (MG == 1) logits_item_split<WT>(P, r, sm);
+    else logits_item_tile<WT, MG>(P, r, sm, lb);
+    wg_signal(ctrl + kSlotInts * C_LDONE);
+    record(n_Z + r, K_ROUTER, t_start);
+  }
   for (;;) {
     __syncthreads();
     if (dynamic) {
@@ -1723,17 +1750,13 @@ void moe_persistent(KParams P) {
     const uint64_t t_start = P.trace ? wall_clock64() : 0;
     if (P.trace && tid == 0) sm.mark[0] = sm.mark[1] = 0;
     int kind = -1;
+    const int item = ticket < n_Z ? ticket : ticket + n_L;  // (router items are not ticketed)
     int i = ticket;
     if (i < n_Z) {
       zero_item(P, i);
       wg_signal(ctrl + kSlotInts * C_ZDONE);
       kind = K_ZERO;
-    } else if ((i -= n_Z) < n_L) {
-      if constexpr (MG == 1) logits_item_split<WT>(P, i, sm);
-      else logits_item_tile<WT, MG>(P, i, sm, lb);
-      wg_signal(ctrl + kSlotInts * C_LDONE);
-      kind = K_ROUTER;
-    } else if ((i -= n_L) < n_K) {
+    } else if ((i -= n_Z) < n_K) {
       if (!(P.phases & PH_IDS_GIVEN) && !logits_seen) {
         if (!wg_wait(ctrl + kSlotInts * C_LDONE, n_L, err, sm)) break;
         logits_seen = true;
@@ -1806,17 +1829,7 @@ void moe_persistent(KParams P) {
         break;
       }
     }
-    if (P.trace && tid == 0 && ticket < P.trace_cap) {
-      unsigned long long *rec = P.trace + 4 * (size_t)ticket;
-      rec[0] = t_start;
-      rec[1] = wall_clock64();
-      // ticket | tile-loop start and end (16-bit offsets from the item start, 10 ns units)
-      const uint32_t m0 = sm.mark[0], m1 = sm.mark[1];
-      const unsigned long long d0 = m0 ? min((uint32_t)(m0 - (uint32_t)t_start), 0xffffu) : 0;
-      const unsigned long long d1 = m1 ? min((uint32_t)(m1 - (uint32_t)t_start), 0xffffu) : 0;
-      rec[2] = (unsigned long long)(uint32_t)ticket | (d0 << 32) | (d1 << 48);
-      rec[3] = ((unsigned long long)blockIdx.x << 32) | (unsigned)kind;
-    }
+    record(item, kind, t_start);
   }
   // The last workgroup out resets the control block for the next call.  Thread 0 made every
   // counter update of this workgroup (the unused prefetched ticket included); once they have

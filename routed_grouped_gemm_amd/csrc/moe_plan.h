@@ -133,9 +133,10 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // words of one per-m-tile counter array (gate/up done, down done), padded to 256 bytes
 inline int ctr_words(const Layout &L) { return (int)align_up((size_t)(L.mt_routed_max + L.n_shmt + 1), 64); }
 
-// Work items of one launch, per phase, in ticket order: Z (clear counters), L (router),
-// K (top-k), SG (shared gate/up), S (scatter); the routed gate/up, down and combine items
-// follow and are counted on the device once the plan exists.
+// Work items of one launch, per phase, in order: Z (clear counters), L (router), K (top-k),
+// SG (shared gate/up), S (scatter); the routed gate/up, down and combine items follow and are
+// counted on the device once the plan exists.  The router items take no ticket (workgroup b
+// runs items b, b + grid, ... first); the others are handed out by ticket in this order.
 struct PhaseCounts {
   int gd_words, hist_words;  // words cleared by Z items: dependency counters, chunk histograms
   int z, l, k, sg, s;

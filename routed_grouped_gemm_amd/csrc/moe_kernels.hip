@@ -80,6 +80,7 @@ struct KParams {
   int phases;
   int bm, tk, gu_cols, dn_cols;
   int n_lt, n_le, n_kt, n_kc, n_shmt, nt_gu, nt_dn, n_comb, mt_cap;
+  int kt_tok;                     // tokens per top-k item
   int ctok;       // tokens per combine item
   int n_Z, n_L, n_K, n_SG, n_S;   // items per static phase (order Z, L, K, SG, S)
   int gd_words, hist_words;       // words cleared by the Z items
@@ -1052,15 +1053,14 @@ __device__ __forceinline__ void topk_group4(const KParams &P, const int (&t)[TPW
   topk_weights<TPW>(P, t, live, lj, ej, ids_lds);
 }
 
-// top-k + softmax for the kTopkTokens tokens of item c.  For E <= 256 a wave handles its 4
-// tokens together, with all of their logits loaded before the first selection.  The loads
-// are unconditional (clamped index, masked after): a load under a lane condition is waited
-// for inside its branch, which would serialise the loads.
-template <class SM>
+// top-k + softmax for the ntok <= 4 * TPW tokens of an item.  For E <= 256 a wave handles
+// its TPW tokens together, with all of their logits loaded before the first selection.  The
+// loads are unconditional (clamped index, masked after): a load under a lane condition is
+// waited for inside its branch, which would serialise the loads.
+template <int TPW, class SM>
 __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, SM &sm) {
   const int tid = otid(), wave = tid >> 6, lane = tid & 63, k = P.k, E = P.E;
   if (E <= 256) {
-    constexpr int TPW = kTopkTokens / kWaves;  // tokens per wave
     float v[TPW][4];
     int t[TPW];
     bool live[TPW];
@@ -1136,18 +1136,21 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
   }
 }
 
-// K item c: top-k of kTopkTokens tokens.  With a single K item (T <= kTopkTokens) the same
-// workgroup builds the plan and scatters; otherwise it adds its per-expert counts to its
-// chunk's histogram (integer atomics: order-independent) and the last K item plans.
+// K item c: top-k of kt_tok tokens.  When all tokens form one scatter chunk (n_kc == 1),
+// the last K item to finish (or the only one) builds the plan and scatters every token;
+// otherwise an item adds its per-expert counts to its chunk's histogram (integer atomics:
+// order-independent), the last K item plans, and scatter items follow.
 template <class SM>
 __device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
   const int tid = otid(), k = P.k, E = P.E;
-  const int t0 = c * kTopkTokens, ntok = min(kTopkTokens, P.T - t0);
+  const int t0 = c * P.kt_tok, ntok = min(P.kt_tok, P.T - t0);
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
   if (P.phases & PH_IDS_GIVEN) {
     for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = checked_id(P.ids[(size_t)t0 * k + q], E);  // caller's input
+  } else if (P.kt_tok == kTopkTokensSmall) {
+    topk_tokens<kTopkTokensSmall / kWaves>(P, t0, ntok, sm);
   } else {
-    topk_tokens(P, t0, ntok, sm);
+    topk_tokens<kTopkTokens / kWaves>(P, t0, ntok, sm);
   }
   __syncthreads();
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
@@ -1155,14 +1158,26 @@ __device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
     wg_signal(P.ctrl + kSlotInts * C_KDONE);
     return;
   }
-  chunk_masks(P, ntok, sm);
-  if (P.n_kt == 1) {
+  if (P.n_kc <= 1) {
+    int nt = ntok;
+    if (P.n_kt > 1) {
+      // every item's ids and weights are stored once the counter shows all n_kt items
+      const int old = wg_signal(P.ctrl + kSlotInts * C_KDONE);
+      if (tid == 0) sm.bcast[2] = (old == P.n_kt - 1) ? 1 : 0;
+      __syncthreads();
+      if (!uni(sm.bcast[2])) return;
+      nt = P.T;
+      for (int q = tid; q < nt * k; q += kThreads) sm.u.r.ids[q] = checked_id(ld_coh(P.ids + q), E);
+      __syncthreads();
+    }
+    chunk_masks(P, nt, sm);
     plan_wg(P, sm, true);
     __syncthreads();
-    chunk_scatter(P, 0, ntok, sm.u.r.scan0, nullptr, sm.u.r.scan1, sm);
+    chunk_scatter(P, 0, nt, sm.u.r.scan0, nullptr, sm.u.r.scan1, sm);
     plan_publish(P, sm.u.r.scan1[E]);
     return;
   }
+  chunk_masks(P, ntok, sm);
   if (P.tk % kTopkTokens == 0) {  // the item lies in one chunk: add its histogram
     const int chunk = t0 / P.tk;
     for (int e = tid; e < E; e += kThreads) {
@@ -1709,7 +1724,6 @@ void moe_persistent(KParams P) {
   const int nparts = min(kTicketParts, (int)gridDim.x), part = ((int)blockIdx.x + (int)blockIdx.x / 8) % nparts;
   int *pctr = ctrl + kSlotInts * (C_PTICKET + part);
   int next = 0;
-  if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // item trace record (moe_forward_ex with a trace buffer); `item` numbers every item of the
   // launch, router items included, in phase order
   auto record = [&](int item, int kind, uint64_t t_start) {
@@ -1737,6 +1751,9 @@ void moe_persistent(KParams P) {
     wg_signal(ctrl + kSlotInts * C_LDONE);
     record(n_Z + r, K_ROUTER, t_start);
   }
+  // (the first ticket is taken after the router items, so the first tickets, the counter
+  // clearing among them, go to workgroups that are free)
+  if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (;;) {
     __syncthreads();
     if (dynamic) {
@@ -1761,7 +1778,7 @@ void moe_persistent(KParams P) {
         if (!wg_wait(ctrl + kSlotInts * C_LDONE, n_L, err, sm)) break;
         logits_seen = true;
       }
-      if (!zero_seen) {  // chunk histograms are cleared by the Z items
+      if (!zero_seen && P.n_kc > 1) {  // chunk histograms are cleared by the Z items
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
       }
@@ -1963,6 +1980,7 @@ moe_status launch(const Call &c) {
   P.dn_cols = L.tiles.dn_cols;
   P.n_lt = L.n_lt;
   P.n_le = L.n_le;
+  P.kt_tok = L.kt_tok;
   P.rt_split = L.tiles.rt_split;
   P.n_kt = L.n_kt;
   P.n_kc = L.n_kc;

@@ -25,6 +25,7 @@ constexpr int kTicketParts = 8;        // ticket counters (see C_PTICKET)
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 256;
 constexpr int kTopkTokens = 16;        // tokens per top-k item (4 per wave)
+constexpr int kTopkTokensSmall = 4;    // ... when all tokens form one scatter chunk (1 per wave)
 constexpr int kMaxChunkTokens = 128;   // tokens per scatter chunk (rank bitmasks: 4 words)
 constexpr int kMaxChunkSlots = 1024;   // (token, slot) pairs per chunk
 constexpr int kCombineUnroll = 2;      // combine: (token, column) pairs per thread in flight
@@ -67,7 +68,8 @@ struct Layout {
   int64_t T;
   int E;
   int n_lt, n_le;        // router items: token tiles x expert blocks
-  int n_kt;              // top-k items (kTopkTokens tokens each)
+  int n_kt;              // top-k items (kt_tok tokens each)
+  int kt_tok;            // tokens per top-k item: kTopkTokensSmall when n_kc == 1, else kTopkTokens
   int n_kc;              // scatter chunks
   int mt_routed_max;     // bound on routed m-tiles
   int n_shmt;            // shared-expert m-tiles
@@ -157,8 +159,12 @@ inline Layout make_layout(const moe_problem *p) {
   L.tiles.rt_split = 1;
   if (L.tiles.mg == 1 && (int64_t)L.n_lt * L.n_le < 64 && p->d > 2048)
     L.tiles.rt_split = (p->d > 4096 && p->d % 512 == 0) ? 4 : 2;
-  L.n_kt = (int)ceil_div(T, kTopkTokens);
   L.n_kc = (int)ceil_div(T, L.tiles.tk);
+  // one scatter chunk: the top-k items take a token per wave (the selection rounds of
+  // several tokens per wave cost more than the extra items), and the last of them plans and
+  // scatters every token; else 16 tokens per item, chunk histograms and scatter items
+  L.kt_tok = L.n_kc <= 1 ? kTopkTokensSmall : kTopkTokens;
+  L.n_kt = (int)ceil_div(T, L.kt_tok);
   const int64_t tk = T * k;
   int64_t bound = tk / bm + (E < tk ? E : tk);
   if (bound > tk) bound = tk;
@@ -201,7 +207,7 @@ inline Layout make_layout(const moe_problem *p) {
 inline PhaseCounts phase_counts(const Layout &L, int phases) {
   PhaseCounts c{};
   const bool ffn = (phases & PH_FFN) != 0, perm = (phases & PH_PERMUTE) != 0;
-  const bool many = L.n_kt > 1;  // one top-k item plans and scatters by itself
+  const bool many = L.n_kc > 1;  // else the last top-k item plans and scatters by itself
   c.gd_words = ffn ? 2 * ctr_words(L) : 0;
   c.hist_words = (perm && many) ? L.n_kc * L.E : 0;
   c.z = (int)ceil_div(c.gd_words + c.hist_words, kZeroPerItem);

@@ -1602,9 +1602,11 @@ __device__ __forceinline__ bool combine_ready(const KParams &P, int c, SM &sm) {
 // combine: out[t] = sum_j w[t,j] * Y[inv_perm[t*k+j]] (+ Y[T*k + t]), float32, slot order.
 // It ends the layer, so latency matters: each thread keeps kCombineUnroll (token, column)
 // pairs in flight, and takes the slots 8 at a time, with all of their weights and row
-// indices loaded before all 8 rows of Y.
-template <int WT>
-__device__ __forceinline__ void combine_item(const KParams &P, int c) {
+// indices loaded before all 8 rows of Y.  The first batch of weights and row indices is
+// loaded before the wait for the down items (they are final once the scatter is done).
+// False on timeout or fault.
+template <int WT, class SM>
+__device__ __forceinline__ bool combine_item(const KParams &P, int c, SM &sm) {
   using A = typename ActT<WT>::type;
   constexpr int VEC = 16 / sizeof(A);
   constexpr int SB = 8;  // slots per batch
@@ -1624,6 +1626,26 @@ __device__ __forceinline__ void combine_item(const KParams &P, int c) {
       for (int z = 0; z < VEC; ++z) acc[z] += w * bf2f(h[z]);
     }
   };
+  float w[UN][SB];
+  int p[UN][SB];
+  auto load_wp = [&](const int (&t)[UN], int j0) {
+#pragma unroll
+    for (int x = 0; x < UN; ++x)
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const size_t at = (size_t)t[x] * k + min(j0 + b, k - 1);
+        w[x][b] = ld_coh(P.wts + at);
+        p[x][b] = ld_coh(P.inv_perm + at);
+      }
+  };
+  {
+    int t[UN];
+#pragma unroll
+    for (int x = 0; x < UN; ++x) t[x] = t0 + min(otid() + x * kThreads, max(npair - 1, 0)) / max(nv, 1);
+    load_wp(t, 0);
+  }
+  if (!combine_ready(P, c, sm)) return false;
+  bool first = true;
   for (int q0 = otid(); q0 < npair; q0 += UN * kThreads) {
     int t[UN], v[UN];
     float acc[UN][VEC];
@@ -1636,16 +1658,8 @@ __device__ __forceinline__ void combine_item(const KParams &P, int c) {
       for (int z = 0; z < VEC; ++z) acc[x][z] = 0.f;
     }
     for (int j0 = 0; j0 < k; j0 += SB) {
-      float w[UN][SB];
-      int p[UN][SB];
-#pragma unroll
-      for (int x = 0; x < UN; ++x)
-#pragma unroll
-        for (int b = 0; b < SB; ++b) {
-          const size_t at = (size_t)t[x] * k + min(j0 + b, k - 1);
-          w[x][b] = ld_coh(P.wts + at);
-          p[x][b] = ld_coh(P.inv_perm + at);
-        }
+      if (!first) load_wp(t, j0);
+      first = false;
       uint4 raw[UN][SB];
 #pragma unroll
       for (int x = 0; x < UN; ++x)
@@ -1675,6 +1689,7 @@ __device__ __forceinline__ void combine_item(const KParams &P, int c) {
       *reinterpret_cast<uint4 *>(out + (size_t)t[x] * P.d + v[x] * VEC) = o;
     }
   }
+  return true;
 }
 
 // ---------------------------------------------------------------------------------
@@ -1839,8 +1854,7 @@ void moe_persistent(KParams P) {
           if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
           zero_seen = true;
         }
-        if (!combine_ready(P, i, sm)) break;
-        combine_item<WT>(P, i);
+        if (!combine_item<WT>(P, i, sm)) break;
         kind = K_COMB;
       } else {
         break;

@@ -249,12 +249,13 @@ constexpr uint64_t kSpinTicks = 200000000ull;  // ~2 s of the 100 MHz wall clock
 // from ~0.1 us to ~0.9 us apart: hundreds of waiting workgroups polling one address at full
 // rate would saturate that address's memory channel and slow every other load.
 // spin_value returns the value it saw (>= target >= 0), or -1 on timeout or fault.
-__device__ __forceinline__ int spin_value(const int *p, int target, int *err) {
+// fast: polls stay ~0.1 us apart (for waits of a few workgroups at the end of the layer).
+__device__ __forceinline__ int spin_value(const int *p, int target, int *err, bool fast = false) {
   int v = ld_relaxed(p);
   if (v >= target) return v;
   const uint64_t t0 = wall_clock64();
   for (int it = 0;; ++it) {
-    if (it < 8) __builtin_amdgcn_s_sleep(4);
+    if (fast || it < 8) __builtin_amdgcn_s_sleep(4);
     else if (it < 32) __builtin_amdgcn_s_sleep(12);
     else __builtin_amdgcn_s_sleep(32);
     v = ld_relaxed(p);
@@ -266,7 +267,9 @@ __device__ __forceinline__ int spin_value(const int *p, int target, int *err) {
     }
   }
 }
-__device__ __forceinline__ bool spin_geq(const int *p, int target, int *err) { return spin_value(p, target, err) >= 0; }
+__device__ __forceinline__ bool spin_geq(const int *p, int target, int *err, bool fast = false) {
+  return spin_value(p, target, err, fast) >= 0;
+}
 
 __device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
   // exact for values with <= 8 significant bits (decoded fp8 values)
@@ -1590,7 +1593,7 @@ __device__ __forceinline__ bool combine_ready(const KParams &P, int c, SM &sm) {
   for (int q = tid; q < nsl + (P.S ? ntok : 0); q += kThreads) {
     const int gm = q < nsl ? P.n_shmt + ld_coh(P.slotmt + (size_t)t0 * k + q) : (t0 + q - nsl) / P.bm;
     const int *ctr = P.dndone + min(max(gm, 0), P.mt_cap - 1);
-    if (ld_relaxed(ctr) < P.nt_dn && !spin_geq(ctr, P.nt_dn, err)) ok = false;
+    if (ld_relaxed(ctr) < P.nt_dn && !spin_geq(ctr, P.nt_dn, err, true)) ok = false;
   }
   if (tid == 0) sm.bcast[1] = 1;
   __syncthreads();

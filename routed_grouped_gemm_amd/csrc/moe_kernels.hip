@@ -808,7 +808,6 @@ __device__ __forceinline__ void plan_wg(const KParams &P, SM &sm, bool from_lds)
     const int base = smt[e], off = soff[e], c = cnt[e];
     for (int mt = 0; mt < mtc[e]; ++mt) st_coh_int4(P.desc + base + mt, make_int4(e, off + mt * P.bm, min(P.bm, c - mt * P.bm), 0));
   }
-  if (tid == 0) st_coh(P.ctrl + kSlotInts * C_NMT, smt[E]);
 }
 
 // an expert id as kept in LDS: out-of-range ids (caller input) become -1 and are reported
@@ -1875,7 +1874,7 @@ void moe_persistent(KParams P) {
     wait_vm0();
     const int old = __hip_atomic_fetch_add(ctrl + kSlotInts * C_EXIT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (int)gridDim.x - 1) {
-      for (int s = C_TICKET; s <= C_NMT; ++s) st_coh(ctrl + kSlotInts * s, 0);
+      for (int s : {C_ZDONE, C_LDONE, C_KDONE, C_SDONE, C_EXIT}) st_coh(ctrl + kSlotInts * s, 0);
       for (int q = 0; q < kTicketParts; ++q) st_coh(ctrl + kSlotInts * (C_PTICKET + q), 0);
       for (int c = 0; c < kPlanCopies; ++c) st_coh(ctrl + plan_flag_word(c), 0);
     }

@@ -35,10 +35,10 @@ constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroin
 // control-block slots (one int32 each, at int index slot * kSlotInts): a poll of one
 // counter never shares a cache line or channel with the ticket counter or another counter.
 // C_PTICKET + p (p < kTicketParts): ticket counter of partition p, see the persistent
-// kernel; C_TICKET and C_PLAN are unused.
+// kernel.  Slots not named here are unused.
 enum CtrlSlot : int {
-  C_MAGIC = 0, C_TICKET = 1, C_ZDONE = 2, C_LDONE = 3, C_KDONE = 4, C_PLAN = 5, C_SDONE = 6,
-  C_DDONE = 7, C_EXIT = 8, C_NMT = 9, C_ERR = 10, C_PTICKET = 16, C_PLANB = 24, C_NSLOTS = kCtrlSlots
+  C_MAGIC = 0, C_ZDONE = 2, C_LDONE = 3, C_KDONE = 4, C_SDONE = 6, C_EXIT = 8, C_ERR = 10,
+  C_PTICKET = 16, C_PLANB = 24, C_NSLOTS = kCtrlSlots
 };
 // C_PLANB .. C_PLANB + 7: copies of the plan flag (n_mt + 1 once the plan is published),
 // eight per slot, 512 bytes apart; workgroup b polls copy b % kPlanCopies

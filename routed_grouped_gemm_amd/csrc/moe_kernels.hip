@@ -1,35 +1,37 @@
 // moe_kernels.hip -- the MoE-layer forward for gfx950 (MI355X), behind the C ABI of moe.h.
 //
-// One persistent kernel runs the whole layer.  Its work items are pulled from an atomic
-// ticket counter in the workspace (the global task queue with an atomic counter of the
-// Weave review, section 2.2; the work-conserving tile scheduler of the FlashMoE
-// explainer, section 四), in this order:
+// One persistent kernel runs the whole layer.  Its work items are pulled from atomic ticket
+// counters in the workspace (the global task queue with an atomic counter of the Weave
+// review, section 2.2; the work-conserving tile scheduler of the FlashMoE explainer,
+// section 四), one counter per partition of the workgroups, in this order:
 //
-//   Z  clear the per-m-tile dependency counters
-//   L  router logits: 16 tokens x 16 experts per item, K split over the 4 waves (MFMA)
-//   K  top-k + softmax over the kept logits for a chunk of tokens, and the chunk's
-//      per-expert histogram; the last K item to finish builds the plan (scan of the
-//      histograms, expert offsets, the m-tile descriptor table)
-//   SG shared-expert gate/up items (need no routing, so they overlap the plan)
-//   S  stable scatter of a chunk: perm / inv_perm
+//   Z  clear the per-m-tile dependency counters (and chunk histograms)
+//   L  router logits: 16 tokens x 16 experts per item, K split over the 4 waves (MFMA);
+//      these take no ticket: workgroup b runs items b, b + grid, ... first
+//   K  top-k + softmax over the kept logits for a group of tokens; the last K item to
+//      finish builds the plan (expert offsets, the m-tile descriptor table) and, for a
+//      batch that is one scatter chunk, scatters it
+//   SG shared-expert gate/up items (need no routing, so they overlap the routing)
+//   S  stable scatter of a chunk: perm / inv_perm (batches of several chunks)
 //   G  gate/up items (m-tile, H columns): gathered token rows x W_gate/W_up, SwiGLU in
 //      registers, H written once
 //   D  down items (m-tile, output columns): H rows x W_down -> Y
 //   C  combine items: out[t] = sum_j w[t,j] * Y[inv_perm[t*k+j]] (+ Y_shared[t]), fixed
 //      slot order, float32, one rounding, no float atomics
 //
-// A work item only ever waits for items with smaller tickets.  Those were taken by
+// A work item only ever waits for items earlier in this order.  Those were taken by
 // workgroups that are running (a workgroup holds at most its current ticket and the next
-// one it prefetched, which is larger), so every wait ends whatever the grid size or how
-// many workgroups are resident.  Every wait is also bounded in time; a timeout sets a
-// fault flag that makes every later wait give up, so the kernel always exits.
+// one it prefetched, which is larger; router items wait for nothing), so every wait ends
+// whatever the grid size or how many workgroups are resident.  Every wait is also bounded
+// in time; a timeout sets a fault flag that makes every later wait give up, so the kernel
+// always exits.
 //
-// Expert tiles: weights are the MFMA A operand (rows = output channels, K contiguous, one
-// 16-byte load per lane straight from HBM into registers, double-buffered), token rows
-// are the B operand (gathered rows copied global -> LDS by the load-to-LDS path, with an
-// XOR swizzle, double-buffered).  This is the operand-swapped form that suits small M
-// (GC-MoE article, "two MMA implementations"): the weight stream, the HBM-bound part, is
-// read exactly once per item and never passes through LDS.
+// Expert tiles: weights are the MFMA A operand (rows = output channels, in a packed
+// fragment layout, one 16-byte load per lane straight from HBM into registers), token rows
+// are the B operand.  This is the operand-swapped form that suits small M (GC-MoE article,
+// "two MMA implementations"): the weight stream, the HBM-bound part, is read once per item
+// and never passes through LDS.  Decode-sized m-tiles (16 rows) read the token rows
+// straight into registers; larger m-tiles stage them in LDS with the load-to-LDS path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1372,9 +1374,9 @@ __device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm, const
 // streamed straight from HBM to registers, so the weight stream is spread evenly over
 // every workgroup and no unit waits for a long one.  A gate/up unit is 16 H columns
 // (wave w: the gate (w < 2) or up fragment over one half of K, the halves added in a
-// fixed order through LDS); a down unit is 64 output channels (wave w: 16 of them over
-// all of K).  Token rows past the tile's end repeat its last row (the same addresses, so
-// the loads coalesce) and are never stored.
+// fixed order through LDS); a down unit is 128 output channels (wave w: 32 of them, two
+// adjacent fragments, over all of K).  Token rows past the tile's end repeat its last row
+// (the same addresses, so the loads coalesce) and are never stored.
 // ---------------------------------------------------------------------------------
 
 // acc[f] of NFR 16-row weight fragments against the same 16 token rows over nsteps

@@ -526,7 +526,7 @@ template <int WT, int MG> struct Core {
 // bytes of each of the three activation staging buffers (separate LDS variables, see Lds3):
 // the expert tile's chunk, or the router tile's on kernels whose router uses the tile core
 template <int WT, int MG> struct ActBuf {
-  using RC = Core<(WT == WF32 ? WF32 : WBF16), 1>;
+  using RC = Core<(WT == WF32 ? WF32 : WBF16), router_groups(MG)>;
   static constexpr int BYTES = (MG > 1 && RC::BUF > Core<WT, MG>::BUF) ? RC::BUF : Core<WT, MG>::BUF;
 };
 
@@ -542,7 +542,7 @@ template <int WT, int MG> struct Smem {
     } r;
     f4 red[kWaves][64];
   } u;
-  int rows[MG * 16];
+  int rows[(MG > router_groups(MG) ? MG : router_groups(MG)) * 16];
   int bcast[4];
   uint32_t mark[2];  // trace: clock at the start and end of the tile loop of this item
 };
@@ -688,11 +688,17 @@ __device__ __forceinline__ void logits_item_split(const KParams &P, int i, SM &s
 template <int WT, int MG, class SM>
 __device__ __forceinline__ void logits_item_tile(const KParams &P, int i, SM &sm, const Lds3 &lb) {
   constexpr int RT = (WT == WF32) ? WF32 : WBF16;
-  constexpr int RMG = 1;  // 16 tokens x 128 experts: enough items to spread over the GPU
+  // 16 * RMG tokens x 64 * NF experts per tile (W_r is read once per tile's tokens), over
+  // part ks of the S = rt_split parts of K (enough items to spread over the GPU); S > 1
+  // writes partial sums that the top-k items add in part order, then the bias
+  constexpr int RMG = router_groups(MG);
   using C = Core<RT, RMG>;
   constexpr int NF = C::NF;
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
-  const int lt = i / P.n_le, le = i % P.n_le;
+  const int S = P.rt_split, ls = S == 4 ? 2 : S == 2 ? 1 : 0;  // (S is 1, 2 or 4: shifts)
+  const int ks = i & (S - 1), tile = i >> ls;
+  const int lt = tile / P.n_le, le = tile % P.n_le;
+  const int kpart = P.d >> ls, kbeg = ks * kpart;
   const int t0 = lt * C::BMR, e0 = le * (64 * NF) + wv * 16 * NF;
   const int m = min(C::BMR, P.T - t0);
   for (int r = tid; r < C::BMR; r += kThreads) sm.rows[r] = t0 + min(r, m - 1);
@@ -703,22 +709,26 @@ __device__ __forceinline__ void logits_item_tile(const KParams &P, int i, SM &sm
 #pragma unroll
   for (int a = 0; a < NF; ++a) {
     const int er = min(e0 + 16 * a + j, P.E - 1);
-    wrow[a] = reinterpret_cast<const char *>(P.wr) + (size_t)er * P.d * asz + g * 16;
+    wrow[a] = reinterpret_cast<const char *>(P.wr) + ((size_t)er * P.d + kbeg) * asz + g * 16;
     sc[a] = nullptr;
   }
   f4 acc[NF][RMG];
-  C::template run<false, 64>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, lb, P.d,
-                             (m + 15) >> 4);
+  C::template run<false, 64>(acc, wrow, sc, reinterpret_cast<const char *>(P.x) + (size_t)kbeg * asz,
+                             (size_t)P.d * asz, sm.rows, lb, kpart, (m + 15) >> 4);
 #pragma unroll
   for (int a = 0; a < NF; ++a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int e = e0 + 16 * a + 4 * g + r;
       if (e >= P.E) continue;
-      const float bv = P.bias ? P.bias[e] : 0.f;
+      const float bv = (P.bias && S == 1) ? P.bias[e] : 0.f;
 #pragma unroll
-      for (int b = 0; b < RMG; ++b)
-        if (b * 16 + j < m) st_coh(P.logits + (size_t)(t0 + b * 16 + j) * P.E + e, acc[a][b][r] + bv);
+      for (int b = 0; b < RMG; ++b) {
+        if (b * 16 + j >= m) continue;
+        const size_t t = (size_t)(t0 + b * 16 + j);
+        if (S == 1) st_coh(P.logits + t * P.E + e, acc[a][b][r] + bv);
+        else st_coh(P.lpart + ((size_t)ks * P.T + t) * P.E + e, acc[a][b][r]);
+      }
     }
   }
 }
@@ -1089,12 +1099,22 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
     }
     asm volatile("" ::: "memory");  // all of the wave's loads are in flight before any is used
     if (S > 1) {
-      for (int ks = 1; ks < S; ++ks) {
+      // parts 1..S-1 loaded together (clamped part index; unused copies are not added)
+      float pp[TPW][4][3];
 #pragma unroll
-        for (int u = 0; u < TPW; ++u)
+      for (int u = 0; u < TPW; ++u)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[u][q] += ld_coh(P.lpart + ((size_t)ks * P.T + t[u]) * E + min(q * 64 + lane, E - 1));
-      }
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int x = 0; x < 3; ++x)
+            pp[u][q][x] = ld_coh(P.lpart + ((size_t)min(x + 1, S - 1) * P.T + t[u]) * E + min(q * 64 + lane, E - 1));
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int x = 0; x < 3; ++x)
+            if (x + 1 < S) v[u][q] += pp[u][q][x];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float bq = P.bias ? P.bias[min(q * 64 + lane, E - 1)] : 0.f;

@@ -25,6 +25,10 @@ constexpr int kTicketParts = 8;        // ticket counters (see C_PTICKET)
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 256;
 constexpr int kTopkTokens = 16;        // tokens per top-k item (4 per wave)
+// router tiles on the tile core (mg > 1): 16-token groups per tile; 4 (64 tokens x 256
+// experts) only in the 128-row kernels, whose registers hold it without spilling, else 1
+// (16 tokens x 128 experts)
+constexpr int router_groups(int mg) { return mg >= 8 ? 4 : 1; }
 constexpr int kTopkTokensSmall = 4;    // ... when all tokens form one scatter chunk (1 per wave)
 constexpr int kMaxChunkTokens = 128;   // tokens per scatter chunk (rank bitmasks: 4 words)
 constexpr int kMaxChunkSlots = 1024;   // (token, slot) pairs per chunk
@@ -58,7 +62,7 @@ struct Tiles {
   int tk;          // tokens per scatter chunk (tk <= 128, tk * k <= 1024)
   int ctok;        // tokens per combine item (1 for small T: more items in parallel)
   int rt_tokens;   // router item: tokens x experts (16 x 16 split over the 4 waves when
-  int rt_experts;  //   mg == 1, else 16 x 128 on the 16-row expert tile core)
+  int rt_experts;  //   mg == 1, else 16 * router_groups(mg) x 64 * NF on the expert tile core)
   int rt_split;    // K splits per router tile (1, 2 or 4): with few tiles, each item takes
                    //   one part of K and the top-k items add the partial sums in order
 };
@@ -125,8 +129,8 @@ inline Tiles choose_tiles(const moe_problem *p) {
   if (t.tk > kMaxChunkTokens) t.tk = kMaxChunkTokens;
   if (t.tk < 1) t.tk = 1;
   t.ctok = p->T > 1024 ? 4 : 1;
-  t.rt_tokens = 16;
-  t.rt_experts = t.mg == 1 ? 16 : 128;
+  t.rt_tokens = t.mg == 1 ? 16 : 16 * router_groups(t.mg);
+  t.rt_experts = t.mg == 1 ? 16 : router_groups(t.mg) == 1 ? 128 : 256;
   return t;
 }
 
@@ -156,9 +160,15 @@ inline Layout make_layout(const moe_problem *p) {
   // trip: with few tiles and a long K, K is split over 2 or 4 items per tile so that each
   // wave needs one chunk (each wave's part of K stays a multiple of 32).  Short K is not
   // split: the router items are the first of the launch, and more of them only start later.
+  // Tile-core router items (mg > 1) split K until there are 256 items or 4 parts; each part
+  // stays a multiple of 128, the longest K chunk of the tile core.
   L.tiles.rt_split = 1;
   if (L.tiles.mg == 1 && (int64_t)L.n_lt * L.n_le < 64 && p->d > 2048)
     L.tiles.rt_split = (p->d > 4096 && p->d % 512 == 0) ? 4 : 2;
+  if (L.tiles.mg > 1)
+    while (L.tiles.rt_split < 4 && (int64_t)L.n_lt * L.n_le * L.tiles.rt_split < 256 &&
+           p->d % (256 * L.tiles.rt_split) == 0)
+      L.tiles.rt_split *= 2;
   L.n_kc = (int)ceil_div(T, L.tiles.tk);
   // one scatter chunk: the top-k items take a token per wave (the selection rounds of
   // several tokens per wave cost more than the extra items), and the last of them plans and

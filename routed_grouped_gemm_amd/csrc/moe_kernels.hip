@@ -854,7 +854,8 @@ __device__ __forceinline__ void chunk_masks(const KParams &P, int ntok, SM &sm) 
 // mto: per-expert m-tile offsets; the slot's m-tile (row r of expert e's rows is in m-tile
 // mto[e] + r / bm) goes to slotmt, and with 16-row m-tiles the slot's token also goes to the
 // m-tile token table
-template <class SM>
+// TOK_ONLY: only the m-tile token table (16-row m-tiles); !WITH_TOK: everything else.
+template <bool TOK_ONLY = false, bool WITH_TOK = true, class SM>
 __device__ __forceinline__ void chunk_scatter(const KParams &P, int c, int ntok, const int *offs, const int *base,
                                               const int *mto, SM &sm) {
   const int tid = otid(), k = P.k, E = P.E, t0 = c * P.tk;
@@ -871,12 +872,16 @@ __device__ __forceinline__ void chunk_scatter(const KParams &P, int c, int ntok,
     }
     const int r = (base ? base[e] : 0) + rank, p = offs[e] + r;
     const int slot = t0 * k + q;
+    const int gm = mto[e] + r / P.bm;
+    if (TOK_ONLY) {
+      st_coh(P.mtok + gm * 16 + (r & 15), t0 + tt);
+      continue;
+    }
     st_coh(P.perm + p, slot);
     st_coh(P.inv_perm + slot, p);
     if (P.phases & PH_FFN) {
-      const int gm = mto[e] + r / P.bm;
       st_coh(P.slotmt + slot, gm);
-      if (P.bm == 16) st_coh(P.mtok + gm * 16 + (r & 15), t0 + tt);
+      if (WITH_TOK && P.bm == 16) st_coh(P.mtok + gm * 16 + (r & 15), t0 + tt);
     }
   }
 }
@@ -1197,8 +1202,17 @@ __device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
     chunk_masks(P, nt, sm);
     plan_wg(P, sm, true);
     __syncthreads();
-    chunk_scatter(P, 0, nt, sm.u.r.scan0, nullptr, sm.u.r.scan1, sm);
-    plan_publish(P, sm.u.r.scan1[E]);
+    if ((P.phases & PH_FFN) && P.bm == 16) {
+      // the gate/up units need only the plan and the m-tile token table: publish those
+      // first, then finish the scatter (perm, inv_perm, slot m-tiles: for the combine)
+      chunk_scatter<true>(P, 0, nt, sm.u.r.scan0, nullptr, sm.u.r.scan1, sm);
+      plan_publish(P, sm.u.r.scan1[E]);
+      chunk_scatter<false, false>(P, 0, nt, sm.u.r.scan0, nullptr, sm.u.r.scan1, sm);
+    } else {
+      chunk_scatter(P, 0, nt, sm.u.r.scan0, nullptr, sm.u.r.scan1, sm);
+      plan_publish(P, sm.u.r.scan1[E]);
+    }
+    wg_signal(P.ctrl + kSlotInts * C_SDONE);  // (the combine waits for the whole scatter)
     return;
   }
   chunk_masks(P, ntok, sm);
@@ -1744,7 +1758,9 @@ void moe_persistent(KParams P) {
   }
   const int n_Z = P.n_Z, n_L = P.n_L, n_K = P.n_K, n_SG = P.n_SG, n_S = P.n_S;
   const bool dyn = (P.phases & (PH_FFN | PH_COMBINE)) != 0;
-  bool zero_seen = false, logits_seen = false, scat_seen = false;
+  bool zero_seen = false, logits_seen = false, scat_seen = false, comb_scat_seen = false;
+  // the combine needs the whole scatter: the S items, or the last K item's for one chunk
+  const int n_S_comb = n_S + ((P.n_kc <= 1 && (P.phases & PH_PERMUTE)) ? 1 : 0);
   int n_mt = -1;
   int step = 0;
   const bool dynamic = P.schedule == 0;
@@ -1870,9 +1886,9 @@ void moe_persistent(KParams P) {
       } else if ((i -= n_G + n_D) < P.n_comb) {
         // the token's rows of Y are final once the down items of their m-tiles are done (the
         // slot m-tiles come from the scatter; the counters are valid once cleared)
-        if (!scat_seen) {
-          if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S, err, sm)) break;
-          scat_seen = true;
+        if (!comb_scat_seen) {
+          if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S_comb, err, sm)) break;
+          comb_scat_seen = true;
         }
         if (!zero_seen) {
           if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;

@@ -1769,13 +1769,14 @@ void moe_persistent(KParams P) {
   // joins partition (b + b / 8) % np: the hardware deals workgroups to the 8 XCDs round
   // robin (b % 8), so every partition draws on all XCDs, and a partition that falls behind
   // near the end still has the whole chip's bandwidth; workgroup b < np joins partition b,
-  // so every partition has a workgroup and every ticket a taker.  Device atomics on one address serialise (~11 ns each), and every workgroup takes
-  // a ticket at start-up and one per item: split over the partitions, neither the start-up
-  // burst nor the steady stream of ticket atomics queues up behind one address.  A ticket is
-  // still only ever taken by a running workgroup, and each partition's workgroups take their
-  // tickets in increasing order while waiting only for smaller tickets, so every wait ends
-  // (induction over the tickets, as with one counter).  Thread 0 keeps the next ticket
-  // prefetched, so the atomic's latency overlaps the current item.
+  // so every partition has a workgroup and every ticket a taker.  Device atomics on one
+  // address serialise (~11 ns each), and every workgroup takes a ticket at start-up and one
+  // per item: split over the partitions, neither the start-up burst nor the steady stream
+  // of ticket atomics queues up behind one address.  A ticket is still only ever taken by a
+  // running workgroup, and each partition's workgroups take their tickets in increasing
+  // order while waiting only for smaller tickets, so every wait ends (induction over the
+  // tickets, as with one counter).  Thread 0 keeps the next ticket prefetched, so the
+  // atomic's latency overlaps the current item.
   const int nparts = min(kTicketParts, (int)gridDim.x), part = ((int)blockIdx.x + (int)blockIdx.x / 8) % nparts;
   int *pctr = ctrl + kSlotInts * (C_PTICKET + part);
   int next = 0;

@@ -1736,7 +1736,7 @@ __device__ __forceinline__ bool combine_item(const KParams &P, int c, SM &sm) {
 
 // register budget per kernel (waves per SIMD): 2 for the narrow tiles, 1 for the widest
 template <int WT, int MG> struct Occ {
-  static constexpr int waves = MG == 1 ? (WT == WFP8 ? 2 : 3) : (MG == 8 || (MG == 4 && WT != WBF16)) ? 1 : 2;
+  static constexpr int waves = MG == 1 ? (WT == WFP8 ? 2 : 3) : (MG >= 8 || (MG == 4 && WT != WBF16)) ? 1 : 2;
 };
 
 template <int WT, int MG>
@@ -1946,8 +1946,12 @@ template <int WT> KernelFn pick_kernel(int mg) {
     case 1: return moe_persistent<WT, 1>;
     case 2: return moe_persistent<WT, 2>;
     case 4: return moe_persistent<WT, 4>;
-    default: return moe_persistent<WT, 8>;
+    default: break;
   }
+  if constexpr (WT != WFP8) {  // (no 160-row fp8 kernel: see choose_tiles)
+    if (mg == 10) return moe_persistent<WT, 10>;
+  }
+  return moe_persistent<WT, 8>;
 }
 
 KernelFn kernel_for(int w_dtype, int mg) {

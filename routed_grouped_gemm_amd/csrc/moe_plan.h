@@ -54,7 +54,7 @@ constexpr int kMagic = 0x4d6f4531;     // "MoE1"
 enum PhaseBits : int { PH_ROUTE = 1, PH_PERMUTE = 2, PH_FFN = 4, PH_COMBINE = 8, PH_IDS_GIVEN = 16 };
 
 struct Tiles {
-  int mg;          // 16-row token groups per m-tile (1, 2, 4 or 8)
+  int mg;          // 16-row token groups per m-tile (1, 2, 4, 8 or 10)
   int bm;          // rows per m-tile = 16 * mg
   int nf;          // 16-row weight fragments per wave (2 when mg == 1, else 4)
   int gu_cols;     // H columns per gate/up item: 4 waves x nf/2 x 16 (16 when mg == 1)
@@ -118,7 +118,11 @@ inline Tiles choose_tiles(const moe_problem *p) {
   const double mean_rows = p->E > 0 ? double(p->T) * p->k / p->E : 0.0;
   // the row count of an expert spreads around the mean by about its square root: pick the
   // tile so that most experts fit in one m-tile (each extra m-tile re-reads the weights)
-  t.mg = mean_rows <= 8 ? 1 : mean_rows <= 20 ? 2 : mean_rows <= 44 ? 4 : 8;
+  // (160-row m-tiles past a mean of 100 rows: at a mean of 128 a 128-row tile leaves half
+  // of the experts a second, nearly empty m-tile that re-reads all of their weights; the
+  // fp8 kernels have no registers left for them)
+  t.mg = mean_rows <= 8 ? 1 : mean_rows <= 20 ? 2 : mean_rows <= 44 ? 4
+       : (mean_rows <= 100 || p->w_dtype == MOE_FP8_E4M3) ? 8 : 10;
   t.bm = 16 * t.mg;
   t.nf = t.mg == 1 ? 2 : 4;
   // mg == 1: small units streamed by single waves (gate/up: 16 columns, the waves split

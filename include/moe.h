@@ -124,11 +124,13 @@ typedef struct {
 } moe_route_out;
 
 /* (host) optional launch controls, for tests and ablations; pass NULL for the defaults.
- * grid_wgs: workgroups of the persistent launch (0 = CUs x occupancy).
+ * grid_wgs: workgroups of the persistent launch (0 = CUs x occupancy; larger values are
+ *           reduced to CUs x occupancy, since some work items are bound to workgroups).
  * trace/trace_bytes: optional device buffer of 32-byte records, one per work item, indexed
- *           by ticket: {start, end} of the 100 MHz device clock (uint64 each), then the
- *           ticket in bits 0-31 with the start and end of the item's MFMA tile loop in bits
- *           32-47 and 48-63 (clock ticks after start; 0 = none), then (workgroup << 32 |
+ *           by item (clearing, router, then ticketed items in phase order): {start, end}
+ *           of the 100 MHz device clock (uint64 each), then the item in bits 0-31 with the
+ *           start and end of the item's MFMA tile loop in bits 32-47 and 48-63 (clock ticks
+ *           after start; 0 = none), then (workgroup << 32 |
  *           item kind); kinds: 0 clear, 1 router,
  *           2 top-k (+ plan), 3 shared gate/up, 4 scatter, 5 gate/up, 6 down, 7 combine.
  *           Items beyond the buffer are not recorded.  NULL (default) records nothing.

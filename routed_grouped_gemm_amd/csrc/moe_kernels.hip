@@ -6,8 +6,8 @@
 // section 四), one counter per partition of the workgroups, in this order:
 //
 //   Z  clear the per-m-tile dependency counters (and chunk histograms)
-//   L  router logits: 16 tokens x 16 experts per item, K split over the 4 waves (MFMA);
-//      these take no ticket: workgroup b runs items b, b + grid, ... first
+//   L  router logits: 16 tokens x 16 experts per item, K split over the 4 waves (MFMA)
+//      (Z and L take no ticket: each workgroup runs its share of them first)
 //   K  top-k + softmax over the kept logits for a group of tokens; the last K item to
 //      finish builds the plan (expert offsets, the m-tile descriptor table) and, for a
 //      batch that is one scatter chunk, scatters it
@@ -19,12 +19,13 @@
 //   C  combine items: out[t] = sum_j w[t,j] * Y[inv_perm[t*k+j]] (+ Y_shared[t]), fixed
 //      slot order, float32, one rounding, no float atomics
 //
-// A work item only ever waits for items earlier in this order.  Those were taken by
-// workgroups that are running (a workgroup holds at most its current ticket and the next
-// one it prefetched, which is larger; router items wait for nothing), so every wait ends
-// whatever the grid size or how many workgroups are resident.  Every wait is also bounded
-// in time; a timeout sets a fault flag that makes every later wait give up, so the kernel
-// always exits.
+// A work item only ever waits for items earlier in this order.  Ticketed items were taken
+// by workgroups that are running (a workgroup holds at most its current ticket and the next
+// one it prefetched, which is larger); the Z and L items, which wait for nothing, are bound
+// to workgroups, and the launch never has more workgroups than can be resident at once, so
+// each of those runs too.  So every wait ends, whatever the grid size.  Every wait is also
+// bounded in time; a timeout sets a fault flag that makes every later wait give up, so the
+// kernel always exits.
 //
 // Expert tiles: weights are the MFMA A operand (rows = output channels, in a packed
 // fragment layout, one 16-byte load per lane straight from HBM into registers), token rows
@@ -1807,8 +1808,19 @@ void moe_persistent(KParams P) {
     wg_signal(ctrl + kSlotInts * C_LDONE);
     record(n_Z + r, K_ROUTER, t_start);
   }
-  // (the first ticket is taken after the router items, so the first tickets, the counter
-  // clearing among them, go to workgroups that are free)
+  // The counter-clearing items take no ticket either: workgroup grid - 1 - b runs items b,
+  // b + grid, ... (the last workgroups, which have router items only when every one has),
+  // so that every top-k item finds a workgroup in the first round of tickets.
+  for (int z = (int)gridDim.x - 1 - (int)blockIdx.x; z < n_Z; z += (int)gridDim.x) {
+    __syncthreads();
+    const uint64_t t_start = P.trace ? wall_clock64() : 0;
+    if (P.trace && tid == 0) sm.mark[0] = sm.mark[1] = 0;
+    zero_item(P, z);
+    wg_signal(ctrl + kSlotInts * C_ZDONE);
+    record(z, K_ZERO, t_start);
+  }
+  // (the first ticket is taken after these items, so the first tickets go to workgroups
+  // that are free)
   if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (;;) {
     __syncthreads();
@@ -1823,13 +1835,9 @@ void moe_persistent(KParams P) {
     const uint64_t t_start = P.trace ? wall_clock64() : 0;
     if (P.trace && tid == 0) sm.mark[0] = sm.mark[1] = 0;
     int kind = -1;
-    const int item = ticket < n_Z ? ticket : ticket + n_L;  // (router items are not ticketed)
+    const int item = ticket + n_Z + n_L;  // (counter-clearing and router items are not ticketed)
     int i = ticket;
-    if (i < n_Z) {
-      zero_item(P, i);
-      wg_signal(ctrl + kSlotInts * C_ZDONE);
-      kind = K_ZERO;
-    } else if ((i -= n_Z) < n_K) {
+    if (i < n_K) {
       if (!(P.phases & PH_IDS_GIVEN) && !logits_seen) {
         if (!wg_wait(ctrl + kSlotInts * C_LDONE, n_L, err, sm)) break;
         logits_seen = true;
@@ -2109,7 +2117,10 @@ moe_status launch(const Call &c) {
   int grid = cus * occ;
   if (c.opts && c.opts->grid_wgs > 0) grid = c.opts->grid_wgs;
   P.schedule = c.opts ? c.opts->schedule : 0;
-  if (P.schedule == 1 && grid > cus * occ) grid = cus * occ;  // static binding needs co-residency
+  // never more workgroups than can be resident at once: the clearing and router items (and,
+  // with the static schedule, every item) are bound to workgroups, so every workgroup of the
+  // launch must be able to run while the others wait
+  if (grid > cus * occ) grid = cus * occ;
   if (grid > n_items && P.schedule == 0) grid = n_items > 0 ? n_items : 1;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kernel_for(p->w_dtype, L.tiles.mg), dim3(grid), dim3(kThreads), 0, c.stream, P);

@@ -145,8 +145,8 @@ inline int ctr_words(const Layout &L) { return (int)align_up((size_t)(L.mt_route
 
 // Work items of one launch, per phase, in order: Z (clear counters), L (router), K (top-k),
 // SG (shared gate/up), S (scatter); the routed gate/up, down and combine items follow and are
-// counted on the device once the plan exists.  The router items take no ticket (workgroup b
-// runs items b, b + grid, ... first); the others are handed out by ticket in this order.
+// counted on the device once the plan exists.  The Z and router items take no ticket (each
+// workgroup runs its share of them first); the others are handed out by ticket in this order.
 struct PhaseCounts {
   int gd_words, hist_words;  // words cleared by Z items: dependency counters, chunk histograms
   int z, l, k, sg, s;

@@ -142,8 +142,8 @@ def cpu_baseline(inp, budget_s=12.0):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of this "
-                                   "build (use --gpus 1)"}))
+        print(json.dumps({"error": "this benchmark measures the layer on one GPU; more than one GPU is not "
+                                   "supported (use --gpus 1)"}))
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration(a.steps)

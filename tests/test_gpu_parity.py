@@ -55,6 +55,8 @@ ADHOC = [
     (19, 160, 512, 256, 8, 2, "bf16", "bf16", 0, False),   # ~40 rows/expert -> 64-row tiles
     (20, 5, 4608, 256, 320, 4, "bf16", "bf16", 0, True),   # E > 256; router K in four parts
     (21, 3, 2560, 256, 24, 3, "bf16", "bf16", 1, True),    # router K in two parts
+    (22, 420, 256, 256, 4, 1, "f32", "f32", 0, True),      # ~105 rows/expert -> 160-row tiles (fp32)
+    (23, 333, 512, 256, 3, 1, "bf16", "bf16", 1, False),   # ~111 rows/expert -> 160-row tiles, ragged
 ]
 
 

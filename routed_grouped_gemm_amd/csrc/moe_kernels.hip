@@ -619,7 +619,7 @@ __device__ __forceinline__ void logits_item_split(const KParams &P, int i, SM &s
   constexpr int KU = Ty<RT>::KU, ASZ = Ty<RT>::ASZ;
   constexpr int CH = 16;  // K steps per chunk
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
-  const int S = P.rt_split, ls = S == 4 ? 2 : S == 2 ? 1 : 0;  // (S is 1, 2 or 4: shifts)
+  const int S = P.rt_split, ls = S == 8 ? 3 : S == 4 ? 2 : S == 2 ? 1 : 0;  // (S: 1, 2, 4 or 8)
   const int ks = i & (S - 1), tile = i >> ls;
   const int lt = tile / P.n_le, le = tile % P.n_le;
   const int t0 = lt * 16, e0 = le * 16;
@@ -696,7 +696,7 @@ __device__ __forceinline__ void logits_item_tile(const KParams &P, int i, SM &sm
   using C = Core<RT, RMG>;
   constexpr int NF = C::NF;
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
-  const int S = P.rt_split, ls = S == 4 ? 2 : S == 2 ? 1 : 0;  // (S is 1, 2 or 4: shifts)
+  const int S = P.rt_split, ls = S == 8 ? 3 : S == 4 ? 2 : S == 2 ? 1 : 0;  // (S: 1, 2, 4 or 8)
   const int ks = i & (S - 1), tile = i >> ls;
   const int lt = tile / P.n_le, le = tile % P.n_le;
   const int kpart = P.d >> ls, kbeg = ks * kpart;
@@ -1077,7 +1077,8 @@ __device__ __forceinline__ void topk_group4(const KParams &P, const int (&t)[TPW
 // its TPW tokens together, with all of their logits loaded before the first selection.  The
 // loads are unconditional (clamped index, masked after): a load under a lane condition is
 // waited for inside its branch, which would serialise the loads.
-template <int TPW, class SM>
+// SMAX: the most parts the router's K can be split into in this kernel
+template <int TPW, int SMAX, class SM>
 __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, SM &sm) {
   const int tid = otid(), wave = tid >> 6, lane = tid & 63, k = P.k, E = P.E;
   if (E <= 256) {
@@ -1106,20 +1107,20 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
     asm volatile("" ::: "memory");  // all of the wave's loads are in flight before any is used
     if (S > 1) {
       // parts 1..S-1 loaded together (clamped part index; unused copies are not added)
-      float pp[TPW][4][3];
+      float pp[TPW][4][SMAX - 1];
 #pragma unroll
       for (int u = 0; u < TPW; ++u)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int x = 0; x < 3; ++x)
+          for (int x = 0; x < SMAX - 1; ++x)
             pp[u][q][x] = ld_coh(P.lpart + ((size_t)min(x + 1, S - 1) * P.T + t[u]) * E + min(q * 64 + lane, E - 1));
 #pragma unroll
       for (int u = 0; u < TPW; ++u)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int x = 0; x < 3; ++x)
+          for (int x = 0; x < SMAX - 1; ++x)
             if (x + 1 < S) v[u][q] += pp[u][q][x];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -1170,7 +1171,7 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
 // the last K item to finish (or the only one) builds the plan and scatters every token;
 // otherwise an item adds its per-expert counts to its chunk's histogram (integer atomics:
 // order-independent), the last K item plans, and scatter items follow.
-template <class SM>
+template <int SMAX, class SM>
 __device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
   const int tid = otid(), k = P.k, E = P.E;
   const int t0 = c * P.kt_tok, ntok = min(P.kt_tok, P.T - t0);
@@ -1178,9 +1179,9 @@ __device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
   if (P.phases & PH_IDS_GIVEN) {
     for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = checked_id(P.ids[(size_t)t0 * k + q], E);  // caller's input
   } else if (P.kt_tok == kTopkTokensSmall) {
-    topk_tokens<kTopkTokensSmall / kWaves>(P, t0, ntok, sm);
+    topk_tokens<kTopkTokensSmall / kWaves, SMAX>(P, t0, ntok, sm);
   } else {
-    topk_tokens<kTopkTokens / kWaves>(P, t0, ntok, sm);
+    topk_tokens<kTopkTokens / kWaves, SMAX>(P, t0, ntok, sm);
   }
   __syncthreads();
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
@@ -1846,7 +1847,7 @@ void moe_persistent(KParams P) {
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
       }
-      topk_item(P, i, sm);
+      topk_item<kMaxRouterSplit(WT == WFP8, MG)>(P, i, sm);
       kind = K_TOPK;
     } else if ((i -= n_K) < n_SG) {
       if (!zero_seen) {

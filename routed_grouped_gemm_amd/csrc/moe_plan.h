@@ -25,6 +25,10 @@ constexpr int kTicketParts = 8;        // ticket counters (see C_PTICKET)
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 256;
 constexpr int kTopkTokens = 16;        // tokens per top-k item (4 per wave)
+// most parts the router's K is split into: 8 on the tile core (mg > 1) except in the fp8
+// kernels, whose registers have no room for the top-k items to load 8 parts at once
+constexpr int kMaxRouterSplit(bool fp8, int mg) { return (mg == 1 || fp8) ? 4 : 8; }
+
 // router tiles on the tile core (mg > 1): 16-token groups per tile; 4 (64 tokens x 256
 // experts) only in the 128-row kernels, whose registers hold it without spilling, else 1
 // (16 tokens x 128 experts)
@@ -63,7 +67,7 @@ struct Tiles {
   int ctok;        // tokens per combine item (1 for small T: more items in parallel)
   int rt_tokens;   // router item: tokens x experts (16 x 16 split over the 4 waves when
   int rt_experts;  //   mg == 1, else 16 * router_groups(mg) x 64 * NF on the expert tile core)
-  int rt_split;    // K splits per router tile (1, 2 or 4): with few tiles, each item takes
+  int rt_split;    // K splits per router tile (1, 2, 4 or 8): with few tiles, each item takes
                    //   one part of K and the top-k items add the partial sums in order
 };
 
@@ -164,13 +168,14 @@ inline Layout make_layout(const moe_problem *p) {
   // trip: with few tiles and a long K, K is split over 2 or 4 items per tile so that each
   // wave needs one chunk (each wave's part of K stays a multiple of 32).  Short K is not
   // split: the router items are the first of the launch, and more of them only start later.
-  // Tile-core router items (mg > 1) split K until there are 256 items or 4 parts; each part
+  // Tile-core router items (mg > 1) split K until there are 256 items or 8 parts; each part
   // stays a multiple of 128, the longest K chunk of the tile core.
   L.tiles.rt_split = 1;
   if (L.tiles.mg == 1 && (int64_t)L.n_lt * L.n_le < 64 && p->d > 2048)
     L.tiles.rt_split = (p->d > 4096 && p->d % 512 == 0) ? 4 : 2;
   if (L.tiles.mg > 1)
-    while (L.tiles.rt_split < 4 && (int64_t)L.n_lt * L.n_le * L.tiles.rt_split < 256 &&
+    while (L.tiles.rt_split < kMaxRouterSplit(p->w_dtype == MOE_FP8_E4M3, L.tiles.mg) &&
+           (int64_t)L.n_lt * L.n_le * L.tiles.rt_split < 256 &&
            p->d % (256 * L.tiles.rt_split) == 0)
       L.tiles.rt_split *= 2;
   L.n_kc = (int)ceil_div(T, L.tiles.tk);

@@ -25,15 +25,15 @@ constexpr int kTicketParts = 8;        // ticket counters (see C_PTICKET)
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 256;
 constexpr int kTopkTokens = 16;        // tokens per top-k item (4 per wave)
+constexpr int kTopkTokensSmall = 4;    // ... when all tokens form one scatter chunk (1 per wave)
 // most parts the router's K is split into: 8 on the tile core (mg > 1) except in the fp8
 // kernels, whose registers have no room for the top-k items to load 8 parts at once
 constexpr int kMaxRouterSplit(bool fp8, int mg) { return (mg == 1 || fp8) ? 4 : 8; }
 
 // router tiles on the tile core (mg > 1): 16-token groups per tile; 4 (64 tokens x 256
-// experts) only in the 128-row kernels, whose registers hold it without spilling, else 1
-// (16 tokens x 128 experts)
+// experts) only in the 128- and 160-row kernels, whose registers hold it without spilling,
+// else 1 (16 tokens x 128 experts)
 constexpr int router_groups(int mg) { return mg >= 8 ? 4 : 1; }
-constexpr int kTopkTokensSmall = 4;    // ... when all tokens form one scatter chunk (1 per wave)
 constexpr int kMaxChunkTokens = 128;   // tokens per scatter chunk (rank bitmasks: 4 words)
 constexpr int kMaxChunkSlots = 1024;   // (token, slot) pairs per chunk
 constexpr int kCombineUnroll = 2;      // combine: (token, column) pairs per thread in flight

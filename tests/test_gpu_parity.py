@@ -57,6 +57,9 @@ ADHOC = [
     (21, 3, 2560, 256, 24, 3, "bf16", "bf16", 1, True),    # router K in two parts
     (22, 420, 256, 256, 4, 1, "f32", "f32", 0, True),      # ~105 rows/expert -> 160-row tiles (fp32)
     (23, 333, 512, 256, 3, 1, "bf16", "bf16", 1, False),   # ~111 rows/expert -> 160-row tiles, ragged
+    (24, 5, 256, 256, 1024, 256, "bf16", "bf16", 1, True),  # largest E and k together
+    (25, 6, 256, 256, 256, 256, "f32", "f32", 0, False),    # k = E = 256: every key of every lane taken
+    (26, 300, 256, 256, 1024, 32, "bf16", "bf16", 0, True), # E = 1024 on the tile core, several top-k chunks
 ]
 
 

@@ -123,6 +123,45 @@ def _ptr(t):
     return t.data_ptr()
 
 
+_ESIZE = {F32: 4, BF16: 2, FP8_E4M3: 1}
+
+
+def _sized(t, numel, esize, name):
+    """The library reads and writes through bare pointers: a tensor smaller than the problem
+    needs, or of another element width, would take it out of bounds, so it is refused here."""
+    if t is None:
+        return
+    if t.numel() < numel or t.element_size() != esize:
+        raise ValueError(f"{name}: needs {numel} elements of {esize} bytes, got {t.numel()} of "
+                         f"{t.element_size()}")
+
+
+def _check_inputs(p: Problem, hidden, w_router, bias, out=None):
+    a = _ESIZE.get(p.act_dtype, 0)
+    _sized(hidden, p.T * p.d, a, "hidden")
+    _sized(w_router, p.E * p.d, a, "w_router")
+    _sized(bias, p.E, 4, "bias")
+    _sized(out, p.T * p.d, a, "out")
+
+
+def _check_weights(p: Problem, weights: dict):
+    """Sizes of the expert (and shared-expert) matrices and, for fp8, their block scales."""
+    w = _ESIZE.get(p.w_dtype, 0)
+    E, d, n = p.E, p.d, p.n
+    sh = p.n_shared > 0
+    for key, rows in (("w_gate", E), ("w_up", E), ("w_down", E), ("sh_gate", 1), ("sh_up", 1), ("sh_down", 1)):
+        if key.startswith("sh_") and not sh:
+            continue
+        _sized(weights.get(key), rows * n * d, w, key)
+    if p.w_dtype == FP8_E4M3:
+        nb = (n // 128) * (d // 128)
+        for key, rows in (("s_gate", E), ("s_up", E), ("s_down", E), ("sh_s_gate", 1), ("sh_s_up", 1),
+                          ("sh_s_down", 1)):
+            if key.startswith("sh_") and not sh:
+                continue
+            _sized(weights.get(key), rows * nb, 4, key)
+
+
 def _stream():
     return torch.cuda.current_stream().cuda_stream
 
@@ -171,6 +210,7 @@ def route(p: Problem, hidden, w_router, bias, ws, want_logits=False):
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     wts = torch.empty((T, k), dtype=torch.float32, device=dev)
     logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    _check_inputs(p, hidden, w_router, bias)
     wp, wb = _ws(ws)
     _check(_load().moe_route(ctypes.byref(p), _ptr(hidden), _ptr(w_router), _ptr(bias), _ptr(ids), _ptr(wts),
                              _ptr(logits), wp, wb, _stream()), "moe_route")
@@ -184,6 +224,7 @@ def permute(p: Problem, ids, ws):
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    _sized(ids, T * k, 4, "ids")
     wp, wb = _ws(ws)
     _check(_load().moe_permute(ctypes.byref(p), _ptr(ids), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv),
                                wp, wb, _stream()), "moe_permute")
@@ -207,6 +248,9 @@ def forward(p: Problem, hidden, w_router, bias, weights, ws, out=None, route_out
     T, k, E, d = p.T, p.k, p.E, p.d
     if out is None:
         out = torch.empty((T, d), dtype=hidden.dtype, device=dev)
+    _check_inputs(p, hidden, w_router, bias, out)
+    if not isinstance(weights, Weights):
+        _check_weights(p, weights)
     W = weights if isinstance(weights, Weights) else make_weights(weights)
     ro = None
     rdict = None
@@ -240,6 +284,7 @@ _MATS = ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down")
 def pack_weights(p: Problem, weights: dict) -> dict:
     """Row-major expert weights -> a new dict whose matrices are in the packed layout
     (moe_pack_weights, on the current stream); scales are passed through unchanged."""
+    _check_weights(p, weights)
     out = dict(weights)
     for key in _MATS:
         if weights.get(key) is not None:

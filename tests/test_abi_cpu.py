@@ -152,3 +152,30 @@ def test_compute_calls_reject_bad_arguments_before_launch(L):
     # workspace init argument checks
     assert L.moe_workspace_init(None, 1 << 20, None) == INVALID
     assert L.moe_workspace_init(fake, 100, None) == INVALID
+
+
+def test_binding_refuses_undersized_tensors():
+    """The binding checks tensor sizes and element widths against the problem before any
+    pointer reaches the library (host tensors here: the check comes first)."""
+    import torch
+    T, d, n, E, k = 4, 256, 256, 8, 2
+    p = moe.problem(T, d, n, E, k)
+    x = torch.zeros(T * d, dtype=torch.bfloat16)
+    wr = torch.zeros(E * d, dtype=torch.bfloat16)
+    W = {key: torch.zeros(E * n * d, dtype=torch.bfloat16) for key in ("w_gate", "w_up", "w_down")}
+    with pytest.raises(ValueError, match="hidden"):
+        moe.forward(p, x[:-1], wr, None, W, None)
+    with pytest.raises(ValueError, match="w_router"):
+        moe.route(p, x, wr.float(), None, None)
+    with pytest.raises(ValueError, match="bias"):
+        moe.forward(p, x, wr, torch.zeros(E, dtype=torch.bfloat16), W, None)
+    with pytest.raises(ValueError, match="w_down"):
+        moe.forward(p, x, wr, None, dict(W, w_down=W["w_down"][:-1]), None)
+    with pytest.raises(ValueError, match="ids"):
+        moe.permute(p, torch.zeros(T * k - 1, dtype=torch.int32), None)
+    p8 = moe.problem(T, d, n, E, k, w="fp8")
+    W8 = {key: torch.zeros(E * n * d, dtype=torch.uint8) for key in ("w_gate", "w_up", "w_down")}
+    W8.update({key: torch.zeros(E * 4, dtype=torch.float32) for key in ("s_gate", "s_up")})
+    W8["s_down"] = torch.zeros(E * 4 - 1, dtype=torch.float32)
+    with pytest.raises(ValueError, match="s_down"):
+        moe.forward(p8, x, wr, None, W8, None)

@@ -182,6 +182,31 @@ moe_status moe_forward_ex(const moe_problem *p, const void *hidden, const void *
                           const moe_route_out *route_out, void *ws, size_t ws_bytes,
                           hipStream_t stream, const moe_launch_options *opts);
 
+/* Bytes of the fixed device scratch that moe_forward_noalloc uses as its workspace. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_forward for callers that cannot allocate device memory: code under hipGraph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Instead of a caller's workspace it
+ * uses a fixed array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB) in device memory inside the
+ * library; every GPU the library runs on holds its own copy until the process ends.  It calls
+ * no hipMalloc or hipFree and allocates nothing else.
+ *   - Arguments, layouts and results are those of moe_forward (packed weights only); results
+ *     are bitwise identical to moe_forward's.
+ *   - A problem whose workspace (moe_workspace_size) exceeds MOE_NOALLOC_SCRATCH_BYTES is
+ *     refused with MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (decode-sized
+ *     batches fit: e.g. T = 16 at d = 2048, n = 512, E = 256, k = 8 needs about 1 MiB).
+ *   - The first call on a device looks up the array's address and enqueues, on `stream`, a
+ *     fill kernel that initialises the whole array; later calls enqueue only the layer.
+ *   - All calls on one GPU share its array, which keeps the last call's contents: calls that
+ *     overlap on one GPU (different streams, not ordered) race and give undefined results.
+ *     Calls on other streams must be ordered after the first call on the device.
+ *   - A device-side wait timeout (possible only when other kernels hold the compute units
+ *     this launch needs) leaves that call's outputs unspecified and is not reported here;
+ *     the array's control block resets itself at the end of every call. */
+moe_status moe_forward_noalloc(const moe_problem *p, const void *hidden, const void *w_router,
+                               const float *bias, const moe_weights *w, void *out,
+                               const moe_route_out *route_out, hipStream_t stream);
+
 /* Converts row-major expert weights to the packed layout (see above), on `stream`: every
  * matrix of src (w_gate, w_up, w_down and, when p->n_shared, sh_gate, sh_up, sh_down) is
  * written, permuted, to the matching pointer of dst, which must not overlap it.  Scale

@@ -22,9 +22,9 @@ import re
 import torch
 
 __all__ = ["MoEError", "problem", "workspace_size", "alloc_workspace", "workspace_init", "route",
-           "permute", "forward", "pack_weights", "last_device_error", "abi_version", "status_string",
+           "permute", "forward", "forward_noalloc", "pack_weights", "last_device_error", "abi_version", "status_string",
            "MoELayer", "LIB_PATH", "HEADER_PATH", "header_functions", "F32", "BF16", "FP8_E4M3",
-           "ROWMAJOR", "PACKED"]
+           "ROWMAJOR", "PACKED", "NOALLOC_SCRATCH_BYTES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
@@ -33,6 +33,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe.h")
 F32, BF16, FP8_E4M3 = 0, 1, 2
 _DT = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 ROWMAJOR, PACKED = 0, 1
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 _LAYOUT = {"rowmajor": ROWMAJOR, "packed": PACKED}
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
            3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP", 5: "MOE_ERR_DEVICE_FAULT"}
@@ -85,13 +86,14 @@ def _load():
     L.moe_permute.argtypes = [P, VP, VP, VP, VP, VP, VP, SZ, VP]
     L.moe_forward.argtypes = [P, VP, VP, VP, ctypes.POINTER(Weights), VP, ctypes.POINTER(RouteOut), VP, SZ, VP]
     L.moe_forward_ex.argtypes = L.moe_forward.argtypes + [ctypes.POINTER(LaunchOptions)]
+    L.moe_forward_noalloc.argtypes = [P, VP, VP, VP, ctypes.POINTER(Weights), VP, ctypes.POINTER(RouteOut), VP]
     L.moe_pack_weights.argtypes = [P, ctypes.POINTER(Weights), ctypes.POINTER(Weights), VP]
     L.moe_last_device_error.argtypes = [VP, VP]
     L.moe_status_string.argtypes = [I]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_abi_version.argtypes = []
     for fn in ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_permute", "moe_forward",
-               "moe_forward_ex", "moe_pack_weights", "moe_last_device_error", "moe_abi_version"):
+               "moe_forward_ex", "moe_forward_noalloc", "moe_pack_weights", "moe_last_device_error", "moe_abi_version"):
         getattr(L, fn).restype = I
     _lib = L
     return L
@@ -275,6 +277,36 @@ def forward(p: Problem, hidden, w_router, bias, weights, ws, out=None, route_out
         code = L.moe_forward(ctypes.byref(p), _ptr(hidden), _ptr(w_router), _ptr(bias), ctypes.byref(W),
                              _ptr(out), ctypes.byref(ro) if ro is not None else None, wp, wb, _stream())
     _check(code, "moe_forward")
+    return (out, rdict) if route_out else out
+
+
+def _route_dict(T, k, E, dev):
+    return dict(topk_ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+                topk_weights=torch.empty((T, k), dtype=torch.float32, device=dev),
+                logits=torch.empty((T, E), dtype=torch.float32, device=dev),
+                counts=torch.empty(E, dtype=torch.int32, device=dev),
+                offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                perm=torch.empty(T * k, dtype=torch.int32, device=dev),
+                inv_perm=torch.empty(T * k, dtype=torch.int32, device=dev))
+
+
+def forward_noalloc(p: Problem, hidden, w_router, bias, weights, out=None, route_out=False):
+    """The whole layer through moe_forward_noalloc: no workspace argument, the library's fixed
+    device scratch instead (see include/moe.h).  Returns out, or (out, dict of routing
+    tensors)."""
+    dev = hidden.device
+    T, k, E, d = p.T, p.k, p.E, p.d
+    if out is None:
+        out = torch.empty((T, d), dtype=hidden.dtype, device=dev)
+    _check_inputs(p, hidden, w_router, bias, out)
+    if not isinstance(weights, Weights):
+        _check_weights(p, weights)
+    W = weights if isinstance(weights, Weights) else make_weights(weights)
+    rdict = _route_dict(T, k, E, dev) if route_out else None
+    ro = RouteOut(*[_ptr(rdict[f[0]]) for f in RouteOut._fields_]) if route_out else None
+    code = _load().moe_forward_noalloc(ctypes.byref(p), _ptr(hidden), _ptr(w_router), _ptr(bias), ctypes.byref(W),
+                                       _ptr(out), ctypes.byref(ro) if ro is not None else None, _stream())
+    _check(code, "moe_forward_noalloc")
     return (out, rdict) if route_out else out
 
 

@@ -88,6 +88,8 @@ struct KParams {
   int n_Z, n_L, n_K, n_SG, n_S;   // items per static phase (order Z, L, K, SG, S)
   int gd_words, hist_words;       // words cleared by the Z items
   int schedule;  // 0 dynamic, 1 static
+  int reset_err;  // 1: the last workgroup out also clears the fault flag (fixed scratch, whose
+                  //    flag no caller can read)
   const void *x, *wr;
   const float *bias;
   const void *wg, *wu, *wd;
@@ -1923,6 +1925,7 @@ void moe_persistent(KParams P) {
     const int old = __hip_atomic_fetch_add(ctrl + kSlotInts * C_EXIT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (int)gridDim.x - 1) {
       for (int s : {C_ZDONE, C_LDONE, C_KDONE, C_SDONE, C_EXIT}) st_coh(ctrl + kSlotInts * s, 0);
+      if (P.reset_err) st_coh(err, 0);
       for (int q = 0; q < kTicketParts; ++q) st_coh(ctrl + kSlotInts * (C_PTICKET + q), 0);
       for (int c = 0; c < kPlanCopies; ++c) st_coh(ctrl + plan_flag_word(c), 0);
     }
@@ -2017,6 +2020,7 @@ struct Call {
   hipStream_t stream;
   int phases;
   const moe_launch_options *opts;
+  int reset_err;
 };
 
 moe_status launch(const Call &c) {
@@ -2118,6 +2122,7 @@ moe_status launch(const Call &c) {
   int grid = cus * occ;
   if (c.opts && c.opts->grid_wgs > 0) grid = c.opts->grid_wgs;
   P.schedule = c.opts ? c.opts->schedule : 0;
+  P.reset_err = c.reset_err;
   // never more workgroups than can be resident at once: the clearing and router items (and,
   // with the static schedule, every item) are bound to workgroups, so every workgroup of the
   // launch must be able to run while the others wait
@@ -2139,6 +2144,42 @@ moe_status check_weights(const moe_problem *p, const moe_weights *w) {
     if (!aligned16(w->sh_gate) || !aligned16(w->sh_up) || !aligned16(w->sh_down)) return MOE_ERR_INVALID_ARGUMENT;
     if (fp8 && (!w->sh_s_gate || !w->sh_s_up || !w->sh_s_down)) return MOE_ERR_INVALID_ARGUMENT;
   }
+  return MOE_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------
+// the allocation-free entry point's workspace: a fixed array in device memory, one copy
+// per GPU (each device that loads the library's code object holds its own, at its own
+// address, until the process ends).  Host code never passes `scratch` itself to a kernel:
+// on the host the name stands for a host-side shadow, not a device address; the device
+// address comes from hipGetSymbolAddress, once per device, and only that is used.
+// ---------------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch[64];  // device address of `scratch` on device i, once initialised
+
+// The device address of this device's scratch (the current device).  The first call on a
+// device looks the address up and enqueues, on `stream`, a fill kernel that puts the whole
+// array in the state moe_workspace_init leaves a workspace in (a kernel, not a memset, so
+// the call may be stream-captured).
+moe_status device_scratch(hipStream_t stream, void **ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    const size_t nwords = (size_t)MOE_NOALLOC_SCRATCH_BYTES / 4;
+    hipLaunchKernelGGL(ws_init_kernel, dim3(4096), dim3(256), 0, stream, static_cast<int *>(p), nwords);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
   return MOE_OK;
 }
 
@@ -2238,6 +2279,45 @@ moe_status moe_forward(const moe_problem *p, const void *hidden, const void *w_r
                        const moe_weights *w, void *out, const moe_route_out *ro, void *ws, size_t ws_bytes,
                        hipStream_t stream) {
   return moe_forward_ex(p, hidden, w_router, bias, w, out, ro, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_forward_noalloc(const moe_problem *p, const void *hidden, const void *w_router, const float *bias,
+                               const moe_weights *w, void *out, const moe_route_out *ro, hipStream_t stream) {
+  moe_status st = validate_problem(p);
+  if (st != MOE_OK) return st;
+  if (make_layout(p).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (p->T == 0) return MOE_OK;  // nothing to read or write; pointers may be NULL
+  if (!hidden || !w_router || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(hidden) || !aligned16(w_router) || !aligned16(out)) return MOE_ERR_INVALID_ARGUMENT;
+  if (out == hidden) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->w_layout != MOE_W_PACKED) return MOE_ERR_UNSUPPORTED;
+  st = check_weights(p, w);
+  if (st != MOE_OK) return st;
+  void *ws = nullptr;
+  st = device_scratch(stream, &ws);
+  if (st != MOE_OK) return st;
+  Call c{};
+  c.p = p;
+  c.hidden = hidden;
+  c.w_router = w_router;
+  c.bias = bias;
+  c.w = w;
+  c.out = out;
+  if (ro) {
+    c.ids_user = ro->topk_ids;
+    c.wts_user = ro->topk_weights;
+    c.logits_user = ro->logits;
+    c.counts_user = ro->counts;
+    c.offsets_user = ro->offsets;
+    c.perm_user = ro->perm;
+    c.invperm_user = ro->inv_perm;
+  }
+  c.ws = ws;
+  c.ws_bytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+  c.stream = stream;
+  c.phases = PH_ROUTE | PH_PERMUTE | PH_FFN | PH_COMBINE;
+  c.reset_err = 1;
+  return launch(c);
 }
 
 moe_status moe_pack_weights(const moe_problem *p, const moe_weights *src, const moe_weights *dst,

@@ -83,6 +83,26 @@ def test_weight_layout_rules(L):
                          None) == UNSUPPORTED
 
 
+def test_noalloc_refuses_oversized_and_invalid_problems_before_any_hip_call(L):
+    """moe_forward_noalloc's fixed scratch has a stated size; larger problems are refused on the
+    host, like invalid ones, before the device is touched."""
+    import re
+    hdr = open(moe.HEADER_PATH).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == moe.NOALLOC_SCRATCH_BYTES
+    VP = ctypes.c_void_p
+    W = moe.Weights(*([1 << 21] * 3 + [None] * 9))
+    big = moe.problem(4096, 2048, 512, 256, 8, layout="packed")
+    assert ws_size(big)[1] > moe.NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(ctypes.byref(big), VP(1 << 20), VP(1 << 20), None, ctypes.byref(W), VP(3 << 20),
+                                 None, None) == TOO_SMALL
+    bad = moe.problem(16, 2000, 512, 256, 8, layout="packed")
+    assert L.moe_forward_noalloc(ctypes.byref(bad), VP(1 << 20), VP(1 << 20), None, ctypes.byref(W), VP(3 << 20),
+                                 None, None) == UNSUPPORTED
+    empty = moe.problem(0, 2048, 512, 256, 8, layout="packed")
+    assert L.moe_forward_noalloc(ctypes.byref(empty), None, None, None, None, None, None, None) == 0
+
+
 def test_pack_weights_rejects_bad_arguments_before_launch(L):
     """moe_pack_weights validates everything on the host (no HIP call on these paths)."""
     VP = ctypes.c_void_p

@@ -58,8 +58,23 @@
  * packed matrices have the same size and the same per-expert offsets; scales and the router
  * are never packed.
  *
+ * This layout departs from a plain [E, d, n] / [E, n, d] (K-major, input-dimension rows)
+ * boundary: expert matrices are output-channel-major ([rows = output channels, K]) and the
+ * compute calls take them packed.  moe_pack_weights is the one conversion, done once at load
+ * time; a caller with [E, d, n] gate/up weights transposes them to [E, n, d] first.
+ *
  * Supported (act dtype, weight dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
- * Shape limits: 1 <= k <= E <= 1024, d and n multiples of 256, T*k < 2^31.
+ * Shape limits: 1 <= k <= E <= 1024, d and n multiples of 256, T*k < 2^31; with fp8
+ * weights also d <= 32768 and n <= 16384 (else MOE_ERR_UNSUPPORTED).
+ *
+ * Execution and co-residency.  The forward is one persistent launch of at most as many
+ * workgroups as the GPU holds at once (compute units x the kernel's occupancy).  Some work
+ * items are bound to workgroups and others wait, on device counters, for items taken before
+ * them, so the launch assumes that all of its workgroups become resident: it should not share
+ * the GPU with kernels that hold compute units for long (other streams, other processes).
+ * Every device-side wait is bounded (about 2 s of the device's 100 MHz clock); a wait that
+ * runs out sets the workspace's fault flag, the launch drains and exits, and
+ * moe_last_device_error reports MOE_ERR_DEVICE_FAULT (the outputs are then unspecified).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -136,10 +151,9 @@ typedef struct {
  *           Items beyond the buffer are not recorded.  NULL (default) records nothing.
  * schedule: 0 = dynamic (work items taken from an atomic queue in the workspace),
  *           1 = static (item i is bound to workgroup i mod grid, like static expert-to-SM
- *               binding in the Weave review, section 4.2),
- *           2 = staged (one launch per phase, the non-fused baseline of the kernel-fusion
- *               comparison page "MoE推理优化：内核融合与分步执行方案对比", scheme B).
- * Every schedule gives bitwise identical results. */
+ *               binding in the Weave review, section 4.2); other values are reserved and
+ *               refused (2: MOE_ERR_UNSUPPORTED, else MOE_ERR_INVALID_ARGUMENT).
+ * Both schedules give bitwise identical results. */
 typedef struct {
   int32_t grid_wgs;
   int32_t schedule;
@@ -147,6 +161,22 @@ typedef struct {
   int64_t trace_bytes;
   int32_t reserved[4];
 } moe_launch_options;
+
+/* (host) the work decomposition moe_forward chooses for a problem (moe_plan_describe). */
+typedef struct {
+  int32_t m_tile_rows;     /* token rows per m-tile of the grouped GEMM: 16, 32, 64, 128 or 160 */
+  int32_t gateup_cols;     /* H columns per gate/up work item                                 */
+  int32_t down_cols;       /* output columns per down work item                              */
+  int32_t router_k_split;  /* parts the router's K is split into (partial logits added in order) */
+  int32_t max_m_tiles;     /* bound on routed m-tiles for any routing (sizes the workspace)   */
+  int32_t reserved[3];
+} moe_plan_info;
+
+/* The tiling moe_forward uses for p (host only, no HIP call), chosen from the per-M bucket
+ * table (vLLM fused-MoE config page, section 03: one tile setting per range of the step's
+ * token count; keyed here by the mean rows per routed expert, T*k/E).  Validation as for
+ * moe_workspace_size. */
+moe_status moe_plan_describe(const moe_problem *p, moe_plan_info *info /* (host) out */);
 
 /* Bytes of workspace a problem needs (host only, no HIP call).  The bound depends on T*k
  * and the shapes, never on the routing.  Returns INVALID_ARGUMENT/UNSUPPORTED like the
@@ -159,13 +189,17 @@ moe_status moe_workspace_size(const moe_problem *p, size_t *bytes /* (host) out 
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Step 1 alone: router logits, top-k and gate weights.  topk_ids and topk_weights are
- * required; logits and bias may be NULL.  Needs a workspace sized for p. */
+ * required; logits and bias may be NULL.  Needs a workspace sized for p: the call runs the
+ * forward's persistent kernel with only its routing phase enabled, and that kernel's queue and
+ * counters live in the workspace. */
 moe_status moe_route(const moe_problem *p, const void *hidden, const void *w_router,
                      const float *bias, int32_t *topk_ids, float *topk_weights, float *logits,
                      void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Step 2 alone: histogram, exclusive scan and stable scatter of given top-k ids
- * (each row of topk_ids must hold k distinct ids in [0, E)).  All outputs required. */
+ * (each row of topk_ids must hold k distinct ids in [0, E)).  All outputs required.  An id
+ * out of range or repeated within a row is ignored or counted once, the outputs are then
+ * unspecified, and moe_last_device_error reports MOE_ERR_DEVICE_FAULT. */
 moe_status moe_permute(const moe_problem *p, const int32_t *topk_ids, int32_t *counts,
                        int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *ws,
                        size_t ws_bytes, hipStream_t stream);

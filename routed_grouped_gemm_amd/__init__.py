@@ -21,7 +21,7 @@ import re
 
 import torch
 
-__all__ = ["MoEError", "problem", "workspace_size", "alloc_workspace", "workspace_init", "route",
+__all__ = ["MoEError", "problem", "workspace_size", "plan_describe", "alloc_workspace", "workspace_init", "route",
            "permute", "forward", "forward_noalloc", "pack_weights", "last_device_error", "abi_version", "status_string",
            "MoELayer", "LIB_PATH", "HEADER_PATH", "header_functions", "F32", "BF16", "FP8_E4M3",
            "ROWMAJOR", "PACKED", "NOALLOC_SCRATCH_BYTES"]
@@ -62,6 +62,12 @@ class RouteOut(ctypes.Structure):
                 ("topk_ids", "topk_weights", "logits", "counts", "offsets", "perm", "inv_perm")]
 
 
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("m_tile_rows", ctypes.c_int32), ("gateup_cols", ctypes.c_int32), ("down_cols", ctypes.c_int32),
+                ("router_k_split", ctypes.c_int32), ("max_m_tiles", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
+
+
 class LaunchOptions(ctypes.Structure):
     _fields_ = [("grid_wgs", ctypes.c_int32), ("schedule", ctypes.c_int32), ("trace", ctypes.c_void_p),
                 ("trace_bytes", ctypes.c_int64), ("reserved", ctypes.c_int32 * 4)]
@@ -82,6 +88,7 @@ def _load():
     P, VP, SZ, I = ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     L.moe_workspace_size.argtypes = [P, ctypes.POINTER(SZ)]
     L.moe_workspace_init.argtypes = [VP, SZ, VP]
+    L.moe_plan_describe.argtypes = [P, ctypes.POINTER(PlanInfo)]
     L.moe_route.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
     L.moe_permute.argtypes = [P, VP, VP, VP, VP, VP, VP, SZ, VP]
     L.moe_forward.argtypes = [P, VP, VP, VP, ctypes.POINTER(Weights), VP, ctypes.POINTER(RouteOut), VP, SZ, VP]
@@ -92,7 +99,7 @@ def _load():
     L.moe_status_string.argtypes = [I]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_abi_version.argtypes = []
-    for fn in ("moe_workspace_size", "moe_workspace_init", "moe_route", "moe_permute", "moe_forward",
+    for fn in ("moe_workspace_size", "moe_workspace_init", "moe_plan_describe", "moe_route", "moe_permute", "moe_forward",
                "moe_forward_ex", "moe_forward_noalloc", "moe_pack_weights", "moe_last_device_error", "moe_abi_version"):
         getattr(L, fn).restype = I
     _lib = L
@@ -186,6 +193,14 @@ def workspace_size(p: Problem) -> int:
     out = ctypes.c_size_t(0)
     _check(_load().moe_workspace_size(ctypes.byref(p), ctypes.byref(out)), "moe_workspace_size")
     return out.value
+
+
+def plan_describe(p: Problem) -> dict:
+    """The tiling the library chooses for problem p (moe_plan_describe): m-tile rows, columns
+    per gate/up and down work item, router K split, bound on routed m-tiles."""
+    info = PlanInfo()
+    _check(_load().moe_plan_describe(ctypes.byref(p), ctypes.byref(info)), "moe_plan_describe")
+    return {f[0]: getattr(info, f[0]) for f in PlanInfo._fields_ if f[0] != "reserved"}
 
 
 def workspace_init(ws: torch.Tensor):

@@ -1,5 +1,5 @@
 // moe_host.cpp -- host-only entry points of the C ABI (no HIP calls): workspace sizing,
-// status strings, ABI version.  Builds with g++ as well as hipcc.
+// tiling description, status strings, ABI version.  Builds with g++ as well as hipcc.
 #include "moe.h"
 #include "moe_plan.h"
 
@@ -10,6 +10,20 @@ moe_status moe_workspace_size(const moe_problem *p, size_t *bytes) {
   const moe_status st = moe::validate_problem(p);
   if (st != MOE_OK) return st;
   *bytes = moe::make_layout(p).total;
+  return MOE_OK;
+}
+
+moe_status moe_plan_describe(const moe_problem *p, moe_plan_info *info) {
+  if (!info) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_status st = moe::validate_problem(p);
+  if (st != MOE_OK) return st;
+  const moe::Layout L = moe::make_layout(p);
+  *info = moe_plan_info{};
+  info->m_tile_rows = L.tiles.bm;
+  info->gateup_cols = L.tiles.gu_cols;
+  info->down_cols = L.tiles.dn_cols;
+  info->router_k_split = L.tiles.rt_split;
+  info->max_m_tiles = L.mt_routed_max;
   return MOE_OK;
 }
 

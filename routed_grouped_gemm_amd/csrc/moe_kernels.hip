@@ -17,7 +17,8 @@
 //      registers, H written once
 //   D  down items (m-tile, output columns): H rows x W_down -> Y
 //   C  combine items: out[t] = sum_j w[t,j] * Y[inv_perm[t*k+j]] (+ Y_shared[t]), fixed
-//      slot order, float32, one rounding, no float atomics
+//      slot order, summed in float32 and rounded once to the output, no float atomics (H and Y
+//      themselves are stored in the activation dtype)
 //
 // A work item only ever waits for items earlier in this order.  Ticketed items were taken
 // by workgroups that are running (a workgroup holds at most its current ticket and the next
@@ -250,7 +251,10 @@ constexpr uint64_t kSpinTicks = 200000000ull;  // ~2 s of the 100 MHz wall clock
 
 // Thread 0 only: wait until *p >= target.  False on timeout or an earlier fault.
 // Polls with relaxed agent-scope loads (an acquire load would invalidate caches on every
-// poll); the caller issues one acquire fence after the wait succeeds.  Polls back off
+// poll).  No fence follows a successful wait: everything the waiter then reads that another
+// workgroup wrote in this launch is read with device-coherent loads (sc1, past this XCD's
+// L2), and the producer's data stores had completed (s_waitcnt vmcnt(0)) before its counter
+// increment was issued, so the data is at the coherence point before the counter.  Polls back off
 // from ~0.1 us to ~0.9 us apart: hundreds of waiting workgroups polling one address at full
 // rate would saturate that address's memory channel and slow every other load.
 // spin_value returns the value it saw (>= target >= 0), or -1 on timeout or fault.
@@ -840,13 +844,16 @@ __device__ __forceinline__ void chunk_masks(const KParams &P, int ntok, SM &sm) 
   __syncthreads();
   for (int q = tid; q < ntok * k; q += kThreads) {
     const int e = sm.u.r.ids[q];
-    if (e >= 0 && e < E) {
+    bool bad = e < 0 || e >= E;
+    if (!bad) {
+      // a token holds an expert at most once: a bit already set is a repeated id (caller
+      // input), counted once and reported
       const int tt = q / k;
-      atomicAdd(&sm.u.r.hist[e], 1);
-      atomicOr(&sm.u.r.mask[e][tt >> 5], 1u << (tt & 31));
-    } else {
-      __hip_atomic_store(P.ctrl + kSlotInts * C_ERR, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t bit = 1u << (tt & 31);
+      if (atomicOr(&sm.u.r.mask[e][tt >> 5], bit) & bit) bad = true;
+      else atomicAdd(&sm.u.r.hist[e], 1);
     }
+    if (bad) __hip_atomic_store(P.ctrl + kSlotInts * C_ERR, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }
@@ -1974,7 +1981,7 @@ KernelFn kernel_for(int w_dtype, int mg) {
 
 struct DevInfo {
   int cus = 0;
-  int occ[3][4] = {};
+  int occ[3][5] = {};  // [weight dtype][m-tile size 16, 32, 64, 128, 160 rows]
 };
 
 std::mutex g_mu;
@@ -1989,7 +1996,7 @@ moe_status device_info(int dev, int w_dtype, int mg, int *cus, int *occ) {
     if (hipDeviceGetAttribute(&D.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MOE_ERR_HIP;
     g_have[dev] = true;
   }
-  const int mi = mg == 1 ? 0 : mg == 2 ? 1 : mg == 4 ? 2 : 3;
+  const int mi = mg == 1 ? 0 : mg == 2 ? 1 : mg == 4 ? 2 : mg == 8 ? 3 : 4;
   int &o = D.occ[w_dtype][mi];
   if (o == 0) {
     int nb = 0;

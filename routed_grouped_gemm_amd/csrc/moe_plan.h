@@ -23,6 +23,7 @@ constexpr int kCtrlSlots = 32;
 constexpr int kCtrlBytes = kCtrlSlots * kSlotInts * 4;  // control block at the start of the workspace
 constexpr int kTicketParts = 8;        // ticket counters (see C_PTICKET)
 constexpr int kMaxE = 1024;
+constexpr int kMaxFp8ScaleBlocks = 128;  // fp8: 128-wide scale blocks along one wave's K range
 constexpr int kMaxK = 256;
 constexpr int kTopkTokens = 16;        // tokens per top-k item (4 per wave)
 constexpr int kTopkTokensSmall = 4;    // ... when all tokens form one scatter chunk (1 per wave)
@@ -106,6 +107,9 @@ inline moe_status validate_problem(const moe_problem *p) {
   if (!ok) return MOE_ERR_UNSUPPORTED;
   if (w == MOE_FP8_E4M3) {
     if (p->scale_block != 128) return MOE_ERR_UNSUPPORTED;
+    // a wave of the 16-row units keeps the block scales of its K range in two lane registers
+    // (128 blocks of 128): gate/up units take half of d, down units all of n
+    if (p->d > kMaxFp8ScaleBlocks * 2 * 128 || p->n > kMaxFp8ScaleBlocks * 128) return MOE_ERR_UNSUPPORTED;
   } else if (p->scale_block != 0) {
     return MOE_ERR_INVALID_ARGUMENT;
   }

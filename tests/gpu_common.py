@@ -12,6 +12,35 @@ from devinputs import out_to_f64, to_device
 TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 5e-2}   # relative Frobenius bound per weight dtype
 
 
+class ExpertPrefetch:
+    """expert(e) for the oracle's forward, which asks for experts in increasing id order (then
+    the shared expert, id E): the float64 views of the next `lookahead` experts are decoded on
+    worker threads while the caller multiplies with the current one.  Only the order of work
+    changes; every value is the InputsView's own."""
+
+    def __init__(self, v, threads=16, lookahead=24):
+        from concurrent.futures import ThreadPoolExecutor
+        self.v = v
+        self.pool = ThreadPoolExecutor(max(1, threads))
+        self.lookahead = lookahead
+        self.pending = {}
+        self.next_id = 0
+        self.decoded = 0
+
+    def _submit_upto(self, last):
+        while self.next_id <= min(last, self.v.E):
+            self.pending[self.next_id] = self.pool.submit(self.v.expert, self.next_id)
+            self.next_id += 1
+
+    def __call__(self, e):
+        self._submit_upto(e + self.lookahead)
+        fut = self.pending.pop(e, None)
+        for old in [q for q in self.pending if q < e]:  # experts the caller skipped (no rows)
+            self.pending.pop(old).cancel()
+        self.decoded += 1
+        return fut.result() if fut is not None else self.v.expert(e)
+
+
 def require_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -75,12 +104,14 @@ def compare_outputs(got, ref, tol, what=""):
     return err, worst
 
 
-def oracle_reference(v, L, ids, gids, mism, tokens=None):
+def oracle_reference(v, L, ids, gids, mism, tokens=None, ref=None):
     """Oracle outputs with the oracle's own routing, except near-tie tokens where the
     GPU legitimately chose differently: those use the GPU's ids (weights from the
-    oracle's logits)."""
+    oracle's logits).  ref: the oracle's outputs of these tokens, if already computed."""
     toks = np.arange(v.x.shape[0]) if tokens is None else np.asarray(tokens)
-    if tokens is None:
+    if ref is not None:
+        ref = np.array(ref, np.float64, copy=True)
+    elif tokens is None:
         ref, _ = oracle.moe_forward_view(v)
     else:
         ref, _, _ = oracle.moe_forward_tokens(v, toks)

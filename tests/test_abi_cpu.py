@@ -53,6 +53,11 @@ def ws_size(p):
     (dict(T=16, d=2048, n=512, E=2048, k=2), UNSUPPORTED),
     (dict(T=16, d=2048, n=512, E=8, k=2, act="f32", w="bf16"), UNSUPPORTED),
     (dict(T=16, d=2048, n=512, E=8, k=2, act="f32", w="fp8"), UNSUPPORTED),
+    # fp8: the 16-row units keep at most 128 scale blocks of their K range per wave
+    (dict(T=16, d=32768, n=16384, E=8, k=2, w="fp8"), 0),
+    (dict(T=16, d=33024, n=512, E=8, k=2, w="fp8"), UNSUPPORTED),
+    (dict(T=16, d=2048, n=16640, E=8, k=2, w="fp8"), UNSUPPORTED),
+    (dict(T=16, d=33024, n=16640, E=8, k=2, w="bf16"), 0),
 ])
 def test_workspace_size_validation(L, kw, code):
     p = moe.problem(**kw)
@@ -60,6 +65,34 @@ def test_workspace_size_validation(L, kw, code):
     assert rc == code
     if code == 0:
         assert size >= 4096 and size % 256 == 0
+
+
+@pytest.mark.parametrize("kw,rows", [
+    (dict(T=16, d=2048, n=512, E=256, k=8), 16),            # decode: mean 0.5 rows per expert
+    (dict(T=512, d=7168, n=2048, E=256, k=8, n_shared=1, w="fp8"), 32),
+    (dict(T=300, d=1024, n=512, E=64, k=6, n_shared=1, w="fp8"), 64),
+    (dict(T=300, d=256, n=512, E=16, k=4, act="f32", w="f32"), 128),
+    (dict(T=4096, d=2048, n=512, E=256, k=8), 160),          # prefill: mean 128
+    (dict(T=4096, d=7168, n=2048, E=256, k=8, n_shared=1, w="fp8"), 128),  # fp8 stops at 128
+])
+def test_plan_describe_reports_the_m_tile(L, kw, rows):
+    info = moe.plan_describe(moe.problem(**kw))
+    assert info["m_tile_rows"] == rows
+    if rows == 16:
+        assert (info["gateup_cols"], info["down_cols"]) == (16, 128)
+    else:
+        assert (info["gateup_cols"], info["down_cols"]) == (128, 256)
+    assert info["router_k_split"] in (1, 2, 4, 8)
+    T, k, E = kw["T"], kw["k"], kw["E"]
+    assert info["max_m_tiles"] >= min(T * k, E)
+
+
+def test_plan_describe_validates(L):
+    bad = moe.problem(16, 2000, 512, 256, 8)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.plan_describe(bad)
+    assert ei.value.code == UNSUPPORTED
+    assert L.moe_plan_describe(ctypes.byref(moe.problem(16, 2048, 512, 256, 8)), None) == INVALID
 
 
 def test_workspace_size_monotone_in_T(L):

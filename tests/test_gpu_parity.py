@@ -43,31 +43,37 @@ def test_forward_named_config(name):
 
 # -- small ragged workloads the oracle runs in full ----------------------------------
 ADHOC = [
-    # seed, T, d, n, E, k, act, w, shared, bias
-    (11, 37, 512, 768, 12, 3, "bf16", "bf16", 0, True),
-    (12, 45, 512, 256, 10, 4, "bf16", "fp8", 1, False),
-    (13, 23, 256, 256, 5, 5, "f32", "f32", 0, False),      # k = E
-    (14, 130, 256, 512, 6, 2, "f32", "f32", 1, True),      # several m-tiles per expert
-    (15, 300, 768, 512, 16, 4, "bf16", "bf16", 1, False),  # mean 75 rows/expert -> 128-row tiles
-    (16, 1, 512, 256, 7, 2, "bf16", "fp8", 0, True),       # T = 1
-    (17, 9, 256, 256, 1, 1, "bf16", "bf16", 0, False),     # E = 1, k = 1
-    (18, 200, 1024, 512, 64, 6, "bf16", "fp8", 1, True),   # ~19 rows/expert -> 32-row tiles
-    (19, 160, 512, 256, 8, 2, "bf16", "bf16", 0, False),   # ~40 rows/expert -> 64-row tiles
-    (20, 5, 4608, 256, 320, 4, "bf16", "bf16", 0, True),   # E > 256; router K in four parts
-    (21, 3, 2560, 256, 24, 3, "bf16", "bf16", 1, True),    # router K in two parts
-    (22, 420, 256, 256, 4, 1, "f32", "f32", 0, True),      # ~105 rows/expert -> 160-row tiles (fp32)
-    (23, 333, 512, 256, 3, 1, "bf16", "bf16", 1, False),   # ~111 rows/expert -> 160-row tiles, ragged
-    (24, 5, 256, 256, 1024, 256, "bf16", "bf16", 1, True),  # largest E and k together
-    (25, 6, 256, 256, 256, 256, "f32", "f32", 0, False),    # k = E = 256: every key of every lane taken
-    (26, 300, 256, 256, 1024, 32, "bf16", "bf16", 0, True), # E = 1024 on the tile core, several top-k chunks
+    # seed, T, d, n, E, k, act, w, shared, bias, m-tile rows the library must choose
+    (11, 37, 512, 768, 12, 3, "bf16", "bf16", 0, True, 32),
+    (12, 45, 512, 256, 10, 4, "bf16", "fp8", 1, False, 32),
+    (13, 23, 256, 256, 5, 5, "f32", "f32", 0, False, 64),      # k = E
+    (14, 130, 256, 512, 6, 2, "f32", "f32", 1, True, 64),      # several m-tiles per expert
+    (15, 300, 768, 512, 16, 4, "bf16", "bf16", 1, False, 128),  # mean 75 rows/expert
+    (16, 1, 512, 256, 7, 2, "bf16", "fp8", 0, True, 16),       # T = 1
+    (17, 9, 256, 256, 1, 1, "bf16", "bf16", 0, False, 32),     # E = 1, k = 1
+    (18, 200, 1024, 512, 64, 6, "bf16", "fp8", 1, True, 32),   # ~19 rows/expert
+    (19, 160, 512, 256, 8, 2, "bf16", "bf16", 0, False, 64),   # ~40 rows/expert
+    (20, 5, 4608, 256, 320, 4, "bf16", "bf16", 0, True, 16),   # E > 256; router K in four parts
+    (21, 3, 2560, 256, 24, 3, "bf16", "bf16", 1, True, 16),    # router K in two parts
+    (22, 420, 256, 256, 4, 1, "f32", "f32", 0, True, 160),     # ~105 rows/expert (fp32)
+    (23, 333, 512, 256, 3, 1, "bf16", "bf16", 1, False, 160),  # ~111 rows/expert, ragged
+    (24, 5, 256, 256, 1024, 256, "bf16", "bf16", 1, True, 16),  # largest E and k together
+    (25, 6, 256, 256, 256, 256, "f32", "f32", 0, False, 16),    # k = E = 256: every key of every lane taken
+    (26, 300, 256, 256, 1024, 32, "bf16", "bf16", 0, True, 32),  # E = 1024 on the tile core, several top-k chunks
+    (27, 300, 1024, 512, 64, 6, "bf16", "fp8", 1, True, 64),   # fp8 64-row tiles, ~28 rows/expert
+    (28, 300, 256, 512, 16, 4, "f32", "f32", 1, False, 128),   # fp32 128-row tiles, 75 rows/expert
+    (29, 400, 512, 256, 16, 4, "bf16", "fp8", 1, True, 128),   # fp8 128-row tiles, 100 rows/expert
+    (30, 250, 512, 512, 8, 4, "f32", "f32", 0, True, 160),     # fp32 160-row tiles, several per expert
 ]
 
 
-@pytest.mark.parametrize("case", ADHOC, ids=lambda c: f"seed{c[0]}_T{c[1]}_E{c[4]}k{c[5]}_{c[7]}_sh{c[8]}")
+@pytest.mark.parametrize("case", ADHOC, ids=lambda c: f"seed{c[0]}_T{c[1]}_E{c[4]}k{c[5]}_{c[7]}_sh{c[8]}_m{c[10]}")
 def test_forward_adhoc(case):
-    seed, T, d, n, E, k, act, w, shared, bias = case
+    seed, T, d, n, E, k, act, w, shared, bias, rows = case
     print(f"[forward parity] adhoc {case}", flush=True)
     inp = synth.make_tiny(seed, T, d, n, E, k, act=act, w=w, shared=shared, bias=bias)
+    # the case exercises the kernel instance of its m-tile size
+    assert moe.plan_describe(moe.problem(T, d, n, E, k, shared, act, w))["m_tile_rows"] == rows
     res = full_parity(inp)
     print(f"  rel_frob={res['err']:.3e} worst_token={res['worst']:.3e}")
 
@@ -117,6 +123,24 @@ def test_permute_exact(T, E, k, mode):
     assert np.array_equal(offsets.cpu().numpy(), ro)
     assert np.array_equal(perm.cpu().numpy(), rp)
     assert np.array_equal(inv.cpu().numpy(), ri)
+
+
+@pytest.mark.parametrize("T,E,k,bad", [(40, 16, 4, "repeat"), (40, 16, 4, "range"), (700, 64, 6, "repeat"),
+                                       (700, 64, 6, "range")])
+def test_permute_reports_invalid_ids(T, E, k, bad):
+    """Caller-given ids that break the contract (an id out of range, an id repeated within a
+    row) are reported as a device fault; the workspace works again after moe_workspace_init."""
+    ids = _permute_case(T, E, k, 5 * T + E, "random")
+    ids[T // 2, 1] = ids[T // 2, 0] if bad == "repeat" else E + 3
+    p = moe.problem(T, 256, 256, E, k)
+    ws = moe.alloc_workspace(p)
+    moe.permute(p, torch.from_numpy(ids).cuda(), ws)
+    assert moe.last_device_error(ws) == 5
+    moe.workspace_init(ws)
+    good = _permute_case(T, E, k, 5 * T + E, "random")
+    counts, offsets, perm, inv = moe.permute(p, torch.from_numpy(good).cuda(), ws)
+    assert moe.last_device_error(ws) == 0
+    assert np.array_equal(perm.cpu().numpy(), oracle.permute(good, E)[2])
 
 
 # -- determinism -----------------------------------------------------------------------

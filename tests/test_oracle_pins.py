@@ -354,7 +354,28 @@ def check_token_subset():
     return []
 
 
-ALL_CHECKS = [check_fp8_decode, check_dequant_blocks, check_widen, check_logits, check_topk_bruteforce,
+def check_rel_frobenius():
+    """Closed forms of ||got - ref||_F / ||ref||_F: a 3-4-5 triangle, a uniform relative
+    scaling, an orthogonal perturbation, a zero output, and a zero reference (whose
+    denominator is taken as 1)."""
+    fails = []
+    ref = np.array([[3.0, 0.0], [0.0, 4.0]])
+    cases = [
+        (ref, ref, 0.0),
+        (ref * 1.25, ref, 0.25),
+        (ref + 0.5 * np.array([[0.0, 4.0], [-3.0, 0.0]]), ref, 0.5),   # |perturbation| = 2.5, |ref| = 5
+        (np.zeros_like(ref), ref, 1.0),
+        (np.array([[0.6, 0.8]]), np.zeros((1, 2)), 1.0),
+        (np.array([[1.0, 2.0, 2.0]]), np.array([[1.0, 2.0, 4.0]]), 2.0 / math.sqrt(21.0)),
+    ]
+    for got, r, want in cases:
+        v = oracle.rel_frobenius(got, r)
+        if not abs(v - want) <= 1e-15 * max(1.0, want):
+            fails.append(f"rel_frobenius {v!r} != {want!r}")
+    return fails
+
+
+ALL_CHECKS = [check_rel_frobenius, check_fp8_decode, check_dequant_blocks, check_widen, check_logits, check_topk_bruteforce,
               check_topk_special, check_weights, check_permute, check_ffn_bruteforce, check_layer_bruteforce,
               check_closed_forms, check_token_subset]
 
@@ -466,6 +487,18 @@ def _mut_logits_no_bias(x, w_router, bias=None):
     return np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
 
 
+def _mut_relfrob_squared(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    den = float((ref * ref).sum())
+    return float(((got - ref) ** 2).sum() / (den if den > 0 else 1.0))
+
+
+def _mut_relfrob_maxabs(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    den = float(np.abs(ref).max()) if ref.size else 0.0
+    return float(np.abs(got - ref).max() / (den if den > 0 else 1.0))
+
+
 _orig_permute = oracle.moe.permute
 
 MUTATIONS = {
@@ -478,6 +511,8 @@ MUTATIONS = {
     "scales_transposed": ("dequant_blocks", _mut_dequant_transposed),
     "shared_dropped": ("combine", _mut_combine_no_shared),
     "bias_dropped": ("router_logits", _mut_logits_no_bias),
+    "rel_frobenius_squared": ("rel_frobenius", _mut_relfrob_squared),
+    "rel_frobenius_max_abs": ("rel_frobenius", _mut_relfrob_maxabs),
 }
 
 
@@ -512,3 +547,18 @@ def test_zipf_bias_fixture_reproduces():
     assert by_rank.tolist() == rec["achieved_counts_by_rank"]
     assert 1.0 <= rec["fitted_exponent"] <= 1.2
     assert by_rank[0] > 0.9 * cfg["T"] and by_rank.min() >= 1
+
+
+def test_prefetched_expert_views_give_the_same_forward():
+    """The parity tests of the large fp8 workload feed the oracle's forward an expert view
+    that decodes upcoming experts on worker threads; its result must be exactly the plain
+    view's."""
+    from gpu_common import ExpertPrefetch
+    inp = synth.make_tiny(5, 37, 256, 256, 9, 3, act="bf16", w="fp8", shared=1, bias=True)
+    v = oracle.InputsView(inp)
+    ref, info = oracle.moe_forward_view(v)
+    pf = ExpertPrefetch(v, threads=3, lookahead=4)
+    out, info2 = oracle.moe_forward(v.x, v.w_router, v.bias, v.k, pf, v.E, lambda: pf(v.E))
+    assert np.array_equal(out, ref)
+    assert np.array_equal(info["perm"], info2["perm"])
+    assert pf.decoded == int((info["counts"] > 0).sum()) + 1

@@ -1,25 +1,36 @@
 """Benchmark of the MoE-layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--T T]
+                    [--configs LIST | --configs none] [--no-cpu-baseline]
 
 A step is one moe_forward call (the whole layer: route, permute, grouped SwiGLU
 GEMM, combine) over one batch of seeded synthetic input already resident in HBM.
-The default workload is the decode-shaped bf16 layer (T=16, d=2048, E=256, top-8,
+The headline workload is the decode-shaped bf16 layer (T=16, d=2048, E=256, top-8,
 n=512).  Weights are rotated over several identical copies so that consecutive
 steps stream weights the 256 MB Infinity Cache does not hold, like consecutive
 layers of a model.  The expert weights are converted to the library's packed
 fragment layout once, with moe_pack_weights, before anything is timed (a
 load-time step, like the fp8 quantisation of the weights).
 
-Prints one JSON line: tokens/s, the roofline of the dominant (and only) kernel
-measured with HIP events on its launch stream, and the CPU oracle timed on a
-bounded sample on this host (cpu_baseline).
+Prints one JSON line: tokens/s of the headline workload, the roofline of the
+dominant (and only) kernel measured with HIP events on its launch stream, the
+CPU oracle timed on a bounded sample on this host (cpu_baseline), and a
+`configs` list with the same measurements for the other workloads: prefill (HBM
+and MFMA fractions), the skewed-load layer under the dynamic queue and under the
+static schedule, and the large fp8 layer at T = 1 and 4096.  `--configs` takes a
+comma-separated list of NAME[@T][:static] entries instead.
 """
-import argparse
-import json
 import os
-import sys
-import time
+
+# the oracle's BLAS uses the cores this process may run on; set before numpy loads
+_CORES = len(os.sched_getaffinity(0))
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ[_v] = str(_CORES)
+
+import argparse  # noqa: E402
+import json  # noqa: E402
+import sys  # noqa: E402
+import time  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -28,6 +39,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 MALL_BYTES = 256 << 20
+DEFAULT_CONFIGS = "prefill_bf16,skewed_bf16,skewed_bf16:static,large_fp8@1,large_fp8@4096"
 
 
 def parse():
@@ -36,7 +48,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode_bf16")
-    ap.add_argument("--T", type=int, default=None, help="token count (large_fp8 sweep)")
+    ap.add_argument("--T", type=int, default=None, help="token count of the headline workload")
+    ap.add_argument("--configs", default=DEFAULT_CONFIGS,
+                    help="other workloads for the configs list: NAME[@T][:static],... or 'none'")
+    ap.add_argument("--config-steps", type=int, default=30, help="timed steps per entry of the configs list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--grid", type=int, default=0)
@@ -85,17 +100,24 @@ def algorithmic(cfg, counts, n_shared):
 KERNEL_SOURCES = ("routed_grouped_gemm_amd/csrc/moe_kernels.hip", "routed_grouped_gemm_amd/csrc/moe_plan.h")
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload
-    (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), or None when there is
-    none or the kernel sources changed since the counters were taken."""
+def kernel_sha():
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    sha = h.hexdigest()[:16]
-    path = os.path.join(ROOT, "profiles", f"moe_persistent_{workload}.md")
+    return h.hexdigest()[:16]
+
+
+def profile_name(workload, T):
+    return f"moe_persistent_{workload}" + ("" if T is None else f"_T{T}")
+
+
+def measured_traffic(workload, T=None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this workload
+    (DRAM read and write requests of the L2s, in 32-byte units), or None when there is none
+    or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", profile_name(workload, T) + ".md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -103,9 +125,18 @@ def measured_traffic(workload):
         if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha"):
             k, v = line.split(":", 1)
             fields[k] = v.strip()
-    if fields.get("kernel_source_sha") != sha or "traffic_bytes_per_launch" not in fields:
+    if fields.get("kernel_source_sha") != kernel_sha() or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
+
+
+def blas_vendor():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        return ",".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info})) or "unknown"
+    except Exception:
+        return "unknown"
 
 
 def cpu_baseline(inp, budget_s=12.0):
@@ -113,11 +144,6 @@ def cpu_baseline(inp, budget_s=12.0):
     (or its first tokens, for the large configs) repeated within a time budget."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
     v = oracle.InputsView(inp)
     T = v.x.shape[0]
     reps, tokens, t0 = 0, 0, time.perf_counter()
@@ -135,8 +161,123 @@ def cpu_baseline(inp, budget_s=12.0):
         tokens = len(toks)
         sample = f"first {len(toks)} of {T} tokens, one by one (every routed and shared expert they touch)"
     dt = time.perf_counter() - t0
-    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 2)}
+    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": _CORES, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2), "blas": blas_vendor(),
+            "threads_env": {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}}
+
+
+class Workloads:
+    """Synthetic inputs, drawn once per weight set (workloads sharing a seed and shapes share
+    weights; the large fp8 sweep shares one weight set over T), kept on the device."""
+
+    def __init__(self):
+        self.host = {}
+        self.dev = {}
+
+    def inputs(self, name, T):
+        import synth
+        cfg = synth.config(name, T)
+        key = (cfg["seed"], cfg["d"], cfg["n"], cfg["E"], cfg["w"], cfg["shared"])
+        if key not in self.host:
+            for k2 in list(self.host):  # one weight set at a time (the fp8 one is 11 GB)
+                del self.host[k2]
+                self.dev.pop(k2, None)
+            full = synth.config(name, synth.config(name)["T_gen"])
+            self.host[key] = synth.make_inputs(full)
+        base = self.host[key]
+        inp = synth.MoEInputs(**{f: getattr(base, f) for f in base.__dataclass_fields__})
+        inp.cfg = cfg
+        inp.hidden = base.hidden[:cfg["T"]]
+        inp.bias = synth.load_zipf_bias(cfg) if cfg.get("zipf") else None
+        return key, cfg, inp
+
+    def device_weights(self, key, inp):
+        from devinputs import to_device
+        if key not in self.dev:
+            self.dev[key] = to_device(inp)[4]
+        return self.dev[key]
+
+
+def measure(wl, name, T, steps, warmup, copies=0, grid=0, schedule=0, want_inputs=False):
+    """Times `steps` launches of one workload; returns a dict of its measurements."""
+    import numpy as np
+    import torch
+
+    import routed_grouped_gemm_amd as moe
+    from devinputs import tensor
+
+    key, cfg, inp = wl.inputs(name, T)
+    W = wl.device_weights(key, inp)
+    p = moe.problem(cfg["T"], cfg["d"], cfg["n"], cfg["E"], cfg["k"], cfg["shared"], cfg["act"], cfg["w"],
+                    layout="packed")
+    x, wr, bias = tensor(inp.hidden), tensor(inp.w_router), tensor(inp.bias)
+    ws = moe.alloc_workspace(p)
+    # routing of this batch (for the algorithmic byte count) from the library itself
+    out, r = moe.forward(p, x, wr, bias, W, ws, route_out=True)
+    torch.cuda.synchronize()
+    assert moe.last_device_error(ws) == 0
+    counts = r["counts"].cpu().numpy()
+    B, F, touched = algorithmic(cfg, counts, cfg["shared"])
+    wbytes = sum(t.numel() * t.element_size() for t in W.values())
+    if not copies:
+        copies = int(min(16, max(2, -(-4 * MALL_BYTES // max(1, min(wbytes, B))))))
+        if wbytes > (8 << 30):
+            copies = 2
+    Ws = [moe.make_weights(W)]
+    keep = [W]
+    for _ in range(copies - 1):
+        Wc = {k2: t.clone() for k2, t in W.items()}
+        keep.append(Wc)
+        Ws.append(moe.make_weights(Wc))
+
+    def step(i):
+        moe.forward(p, x, wr, bias, Ws[i % copies], ws, out=out, grid_wgs=grid, schedule=schedule)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert moe.last_device_error(ws) == 0, "device fault flag set during the timed steps"
+    per = np.array([s.elapsed_time(e) * 1e3 for s, e in ev])  # us per launch
+    avg_us = float(per.mean())
+    mfma = "bf16" if cfg["w"] == "fp8" else cfg["w"]   # fp8 weights are decoded to bf16 for the MFMA
+    peak_mfma = MFMA_PEAK_TFLOPS[mfma]
+    gbs = B / (avg_us * 1e-6) / 1e9
+    tfl = F / (avg_us * 1e-6) / 1e12
+    t_hbm, t_mfma = B / (HBM_PEAK_GBS * 1e9), F / (peak_mfma * 1e12)
+    traffic = measured_traffic(name, None if T is None or name != "large_fp8" else T)
+    res = dict(workload=name, T=cfg["T"], schedule="static" if schedule == 1 else "dynamic",
+               m_tile_rows=moe.plan_describe(p)["m_tile_rows"], experts_touched=touched,
+               p50_us=round(float(np.percentile(per, 50)), 2), p99_us=round(float(np.percentile(per, 99)), 2),
+               avg_launch_us=round(avg_us, 2), steps=steps, wall_s=wall,
+               tokens_per_s=round(cfg["T"] / (avg_us * 1e-6), 1),
+               GB_s=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+               TFLOP_s=round(tfl, 2), mfma_dtype=mfma, mfma_frac=round(tfl / peak_mfma, 4),
+               roofline_bound="hbm" if t_hbm >= t_mfma else "mfma",
+               roofline_time_frac=round(max(t_hbm, t_mfma) / (avg_us * 1e-6), 4),
+               bytes_per_launch=int(B), flops_per_launch=int(F), traffic=traffic,
+               traffic_over_algorithmic=round(traffic / B, 3) if traffic else None,
+               weight_copies_rotated=copies)
+    del keep, Ws, ws, out, r
+    torch.cuda.empty_cache()
+    if want_inputs:
+        return res, cfg, inp
+    return res
+
+
+def parse_entry(e):
+    static = e.endswith(":static")
+    e = e[:-len(":static")] if static else e
+    name, _, t = e.partition("@")
+    return name, (int(t) if t else None), static
 
 
 def main():
@@ -148,98 +289,53 @@ def main():
     if a.copy_calibration:
         copy_calibration(a.steps)
         return
-    import numpy as np
-    import torch
-
     import routed_grouped_gemm_amd as moe
-    import synth
-    from devinputs import to_device
 
     if not os.path.exists(moe.LIB_PATH):
-        from routed_grouped_gemm_amd import build as b
-        b.build()
-    cfg = synth.config(a.config, a.T)
-    inp = synth.make_inputs(cfg)
-    p, x, wr, bias, W = to_device(inp)
-    ws = moe.alloc_workspace(p)
-
-    # routing of this batch (for the algorithmic byte count) from the library itself
-    out, r = moe.forward(p, x, wr, bias, W, ws, route_out=True)
-    torch.cuda.synchronize()
-    assert moe.last_device_error(ws) == 0
-    counts = r["counts"].cpu().numpy()
-    B, F, touched = algorithmic(cfg, counts, cfg["shared"])
-
-    wbytes = sum(t.numel() * t.element_size() for t in W.values())
-    copies = a.copies or int(min(16, max(2, -(-4 * MALL_BYTES // max(1, min(wbytes, B))))))
-    if cfg["w"] == "fp8" and wbytes > (8 << 30):
-        copies = max(2, min(copies, 2))
-    Ws = [moe.make_weights(W)]
-    keep = [W]
-    for _ in range(copies - 1):
-        Wc = {k2: t.clone() for k2, t in W.items()}
-        keep.append(Wc)
-        Ws.append(moe.make_weights(Wc))
-    out = torch.empty((cfg["T"], cfg["d"]), dtype=x.dtype, device="cuda")
-
-    def step(i):
-        moe.forward(p, x, wr, bias, Ws[i % copies], ws, out=out, grid_wgs=a.grid, schedule=a.schedule)
-
-    for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    K = a.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record()
-        step(i)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    assert moe.last_device_error(ws) == 0, "device fault flag set during the timed steps"
-    per = np.array([s.elapsed_time(e) * 1e3 for s, e in ev])  # us per launch
-    avg_us = float(per.mean())
-    T = cfg["T"]
-    value = T * K / wall
-    gbs = B / (avg_us * 1e-6) / 1e9
-    tfl = F / (avg_us * 1e-6) / 1e12
-    peak_mfma = MFMA_PEAK_TFLOPS["bf16" if cfg["w"] == "fp8" else cfg["w"]]
-    t_hbm = B / (HBM_PEAK_GBS * 1e9)
-    t_mfma = F / (peak_mfma * 1e12)
-    if t_hbm >= t_mfma:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        raise SystemExit(f"{moe.LIB_PATH} is not built: run `python -m routed_grouped_gemm_amd.build` first")
+    wl = Workloads()
+    head, cfg, inp = measure(wl, a.config, a.T, a.steps, a.warmup, copies=a.copies, grid=a.grid,
+                             schedule=a.schedule, want_inputs=True)
+    roof = {"bound": head["roofline_bound"]}
+    if head["roofline_bound"] == "hbm":
+        roof.update(achieved=head["GB_s"], peak=HBM_PEAK_GBS, unit="GB/s", frac=head["hbm_frac"])
     else:
-        roof = {"bound": "mfma", "achieved": round(tfl, 2), "peak": peak_mfma, "unit": "TFLOP/s",
-                "frac": round(tfl / peak_mfma, 4)}
-    traffic = measured_traffic(cfg["name"])
-    roof["traffic"] = traffic
-    roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1)"
-    if traffic:
-        roof["traffic_over_algorithmic"] = round(traffic / B, 3)
-    roof["bytes_per_launch"] = int(B)
-    roof["flops_per_launch"] = int(F)
-    roof["kernel"] = "moe_persistent"
-    roof["avg_launch_us"] = round(avg_us, 2)
-    roof["roofline_time_frac"] = round(max(t_hbm, t_mfma) / (avg_us * 1e-6), 4)
+        roof.update(achieved=head["TFLOP_s"], peak=MFMA_PEAK_TFLOPS[head["mfma_dtype"]], unit="TFLOP/s",
+                    frac=head["mfma_frac"])
+    roof.update(traffic=head["traffic"],
+                traffic_unit="HBM bytes per launch (rocprofv3 TCC_EA0_RDREQ_DRAM_32B_sum + "
+                             "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum, x32 bytes; copy-calibrated factor 1.0)",
+                traffic_over_algorithmic=head["traffic_over_algorithmic"],
+                bytes_per_launch=head["bytes_per_launch"], flops_per_launch=head["flops_per_launch"],
+                kernel="moe_persistent", avg_launch_us=head["avg_launch_us"],
+                roofline_time_frac=head["roofline_time_frac"], mfma_frac=head["mfma_frac"])
     res = {
         "metric": "MoE-layer tokens/sec + % roofline (HBM GB/s decode, MFMA TFLOP/s prefill)",
-        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": a.warmup,
-        "ms_per_step": round(wall * 1e3 / K, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if cfg["act"] == "f32" else "bf16", "data": "synthetic",
-        "config": {"workload": cfg["name"], "T": T, "d": cfg["d"], "E": cfg["E"], "k": cfg["k"], "n": cfg["n"],
-                   "shared_experts": cfg["shared"], "act": cfg["act"], "weights": cfg["w"],
+        "value": round(cfg["T"] * a.steps / head["wall_s"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(head["wall_s"] * 1e3 / a.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if cfg["act"] == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "T": cfg["T"], "d": cfg["d"], "E": cfg["E"], "k": cfg["k"],
+                   "n": cfg["n"], "shared_experts": cfg["shared"], "act": cfg["act"], "weights": cfg["w"],
                    "weight_layout": "packed (moe_pack_weights at load time)",
-                   "experts_touched": touched, "weight_copies_rotated": copies, "parallelism": "none (1 GPU)"},
-        "latency_us": {"p50": round(float(np.percentile(per, 50)), 2),
-                       "p99": round(float(np.percentile(per, 99)), 2)},
-        "tflops": round(tfl, 3),
+                   "experts_touched": head["experts_touched"], "m_tile_rows": head["m_tile_rows"],
+                   "weight_copies_rotated": head["weight_copies_rotated"], "parallelism": "none (1 GPU)"},
+        "latency_us": {"p50": head["p50_us"], "p99": head["p99_us"]},
+        "tflops": head["TFLOP_s"],
         "roofline": roof,
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp)
+    if a.configs and a.configs != "none":
+        entries = []
+        for e in a.configs.split(","):
+            name, T, static = parse_entry(e.strip())
+            r = measure(wl, name, T, a.config_steps, 3, schedule=1 if static else 0)
+            r.pop("wall_s")
+            entries.append(r)
+            print(f"[bench] {name} T={r['T']} {r['schedule']}: {r['avg_launch_us']} us, "
+                  f"hbm {r['hbm_frac']}, mfma {r['mfma_frac']}", file=sys.stderr, flush=True)
+        res["configs"] = entries
     print(json.dumps(res), flush=True)
 
 

@@ -64,8 +64,10 @@
  * time; a caller with [E, d, n] gate/up weights transposes them to [E, n, d] first.
  *
  * Supported (act dtype, weight dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
- * Shape limits: 1 <= k <= E <= 1024, d and n multiples of 256, T*k < 2^31; with fp8
- * weights also d <= 32768 and n <= 16384 (else MOE_ERR_UNSUPPORTED).
+ * Shape limits: 1 <= k <= E <= 1024, d and n multiples of 256, T*k < 2^31, hidden
+ * (T*d) and the expert intermediate (T*k + n_shared*T rows of n) each below 4 GB in the
+ * activation dtype; with fp8 weights also d <= 32768 and n <= 16384 (else
+ * MOE_ERR_UNSUPPORTED).
  *
  * Execution and co-residency.  The forward is one persistent launch of at most as many
  * workgroups as the GPU holds at once (compute units x the kernel's occupancy).  Some work
@@ -88,7 +90,7 @@ extern "C" {
 
 typedef struct ihipStream_t *hipStream_t;
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -184,7 +186,7 @@ moe_status moe_plan_describe(const moe_problem *p, moe_plan_info *info /* (host)
 moe_status moe_workspace_size(const moe_problem *p, size_t *bytes /* (host) out */);
 
 /* Clears the workspace's control block (a fill kernel on `stream`).  Call once after
- * allocating a workspace, and again after a MOE_ERR_DEVICE_FAULT.  Needs at least 131072
+ * allocating a workspace, and again after a MOE_ERR_DEVICE_FAULT.  Needs at least 196608
  * bytes. */
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 

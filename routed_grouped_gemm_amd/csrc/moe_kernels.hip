@@ -59,6 +59,8 @@ __device__ __forceinline__ uint4 ld_stream16(const void *p) {
 
 enum : int { WF32 = 0, WBF16 = 1, WFP8 = 2 };
 
+constexpr int kCpolNt = 2;  // cache policy of a buffer load: nontemporal (streamed once)
+
 // KU: K elements per 16-byte weight load of one lane; WSZ/ASZ: weight/activation bytes
 template <int WT> struct Ty;
 template <> struct Ty<WF32> { static constexpr int KU = 16, WSZ = 4, ASZ = 4; };
@@ -91,6 +93,8 @@ struct KParams {
   int schedule;  // 0 dynamic, 1 static
   int reset_err;  // 1: the last workgroup out also clears the fault flag (fixed scratch, whose
                   //    flag no caller can read)
+  int late;       // 1: gate/up and down items from the per-XCD queues, grouped order (see the kernel)
+  int group_m;    // late phase: m-tiles per group
   const void *x, *wr;
   const float *bias;
   const void *wg, *wu, *wd;
@@ -179,24 +183,29 @@ __device__ __forceinline__ void lds_barrier() {
 // tell that a read of one buffer does not depend on a DMA still filling another, and does
 // not wait for the prefetches before every LDS read.
 struct Lds3 {
-  char *b0, *b1, *b2;
+  char *b0, *b1, *b2, *b3;  // (b3: four-stage kernels only)
 };
 
-// 16 bytes per lane, global -> LDS; lane l lands at lds_base + 16*l (lds_base uniform).
-// COH selects the device-coherent cache policy (SC1) for data written in this launch.
-// Written as inline assembly on purpose: the compiler tracks the builtin form as an
-// asynchronous LDS write and then makes every later LDS read wait for all outstanding
-// vector memory operations (prefetches included), which serialises the K pipeline.  Here
-// the waits are explicit instead: a chunk's DMA is complete once the issuing wave has
-// waited for it (vmcnt) and passed the workgroup barrier.  No VGPR is written, so no
-// register can be reused under an in-flight load; M0 is bound through its constraint.
+__device__ __forceinline__ char *stage_buf(const Lds3 &lb, int st) {
+  return st == 0 ? lb.b0 : st == 1 ? lb.b1 : st == 2 ? lb.b2 : lb.b3;
+}
+
+// 16 bytes per lane, global -> LDS, as a buffer load: lane l reads base + voff (its own
+// offset) + soff (uniform) and lands at lds_base + 16*l (lds_base uniform).  COH selects the
+// device-coherent cache policy (SC1) for data written in this launch.  The compiler counts
+// these loads like any other (its vmcnt waits stay exact) and, with the stage buffers as
+// separate LDS variables, makes an LDS read wait only for loads into the buffer it reads;
+// with the offsets in loop-invariant and scalar registers, no vector register is rewritten
+// per stage.
+constexpr int kCpolSc1 = 16;  // cache policy: device-coherent (SC1)
 template <bool COH>
-__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
-  const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)reinterpret_cast<uintptr_t>(lds_base));
-  if constexpr (COH)
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc1" ::"v"(g), "{m0}"(m0v) : "memory");
-  else
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0v) : "memory");
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, void *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds_base, 16, voff, soff, 0,
+                                           COH ? kCpolSc1 : 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
 }
 
 __device__ __forceinline__ int ld_relaxed(const int *p) {
@@ -368,7 +377,7 @@ template <int WT, int MG> struct Core {
         for (int a = 0; a < NF; ++a) s[a] = sc[a][c * BPC + blk];
 #pragma unroll
         for (int b0 = 0; b0 < MG; b0 += MGC) {
-          if (FULL || b0 < ngroups) {
+          if (FULL || b0 == 0 || b0 < ngroups) {
             f4 tmp[NF][MGC];
 #pragma unroll
             for (int a = 0; a < NF; ++a)
@@ -379,7 +388,7 @@ template <int WT, int MG> struct Core {
               const int f = blk * 2 + ff;
 #pragma unroll
               for (int b = 0; b < MGC; ++b) {
-                if (FULL || b0 + b < ngroups) {
+                if (FULL || b0 + b == 0 || b0 + b < ngroups) {
                   const int r = (b0 + b) * 16 + j;
                   const int c0 = f * 8 + 2 * g;
                   const uint4 a0 = *reinterpret_cast<const uint4 *>(A + r * RB + ((c0 ^ (r & (NCOL - 1))) << 4));
@@ -397,17 +406,28 @@ template <int WT, int MG> struct Core {
         }
       }
     } else {
+      // the activation operands of the FL * MG (step, group) pairs, read from LDS LA pairs
+      // ahead of their MFMAs (an LDS read consumed at once would expose its latency before
+      // every group's four MFMAs); every read is unconditional (rows past the tile's end
+      // repeat its last row), only the MFMAs of absent groups are skipped
+      constexpr int NP = FL * MG, LA = NP < 3 ? NP : 3;
+      auto rd = [&](int t) {
+        const int f = t / MG, b = t % MG, r = b * 16 + j, c0 = f * 4 + g;
+        return *reinterpret_cast<const uint4 *>(A + r * RB + ((c0 ^ (r & (NCOL - 1))) << 4));
+      };
+      uint4 av[LA];
 #pragma unroll
-      for (int f = 0; f < FL; ++f) {
+      for (int t = 0; t < LA; ++t) av[t] = rd(t);
 #pragma unroll
-        for (int b = 0; b < MG; ++b) {
-          if (FULL || b < ngroups) {
-            const int r = b * 16 + j;
-            const int c0 = f * 4 + g;
-            const uint4 av = *reinterpret_cast<const uint4 *>(A + r * RB + ((c0 ^ (r & (NCOL - 1))) << 4));
+      for (int t = 0; t < NP; ++t) {
+        const int f = t / MG, b = t % MG;
+        const uint4 cur = av[t % LA];
+        if (t + LA < NP) av[t % LA] = rd(t + LA);
+        // (group 0 always exists: its MFMAs run unconditionally, so the compiler sees every
+        // weight register of the stage consumed, its load complete, on every path)
+        if (FULL || b == 0 || b < ngroups) {
 #pragma unroll
-            for (int a = 0; a < NF; ++a) acc[a][b] = mfma_step<WT>(W[a][f], av, av, acc[a][b]);
-          }
+          for (int a = 0; a < NF; ++a) acc[a][b] = mfma_step<WT>(W[a][f], cur, cur, acc[a][b]);
         }
       }
     }
@@ -429,42 +449,53 @@ template <int WT, int MG> struct Core {
 #pragma unroll
       for (int b = 0; b < MG; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
-    const char *asrc[NDMA];
+    // activation rows: one buffer resource at abase, a per-lane offset per load (the row's
+    // 32-bit offset: every activation tensor is below 4 GB) and the chunk offset
+    const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(abase);
+    uint32_t aoff[NDMA];
 #pragma unroll
     for (int s = 0; s < NDMA; ++s) {
       const int q = s * kWaves + wv;
       const int r = min(q * RPK + lane / NCOL, BMR - 1);  // (clamped for waves without DMA)
       const int col = (lane % NCOL) ^ (r & (NCOL - 1));
-      asrc[s] = abase + (size_t)rows[r] * arow_bytes + col * 16;
+      aoff[s] = (uint32_t)((size_t)rows[r] * arow_bytes + col * 16);
     }
-    // Prefetches past the last chunk still issue, from one fixed address (a single cache
-    // line for the whole wave), so every pipeline stage has the same memory operations:
-    // the wait counts stay constant and the compiler's register scoreboard stays exact
-    // across the loop's back edge (a conditional prefetch makes it wait for everything).
-    // The weight pointers are laundered through empty asm: the compiler can then no longer
-    // prove the weights unchanging, so it keeps each prefetch between the barriers (memory
-    // clobbers) of its own pipeline stage instead of moving it across stages, which would
-    // break the per-stage wait counts.
-    const char *wr[NF];
+    // Prefetches past the last chunk still issue, so every pipeline stage has the same memory
+    // operations: the wait counts stay constant and the compiler's register scoreboard stays
+    // exact across the loop's back edge (a conditional prefetch makes it wait for everything).
+    // Weight loads are buffer loads: one resource per fragment, based at lane 0's address of
+    // that fragment (the fragments of a wave may lie in different matrices: gate and up), a
+    // loop-invariant per-lane offset and the chunk offset in a scalar register, so no vector
+    // register holds a per-stage address (the compiler cannot prove such a temporary free of
+    // pending loads after the loop's back edge, and would wait for every outstanding load
+    // before reusing it).  Lane 0 holds a fragment's lowest address (an expert fragment's
+    // lanes are 16 bytes apart; a router fragment's lanes step through its 16 rows, clamped
+    // to the last expert), so every offset is small and non-negative.
+    __amdgpu_buffer_rsrc_t wrsrc[NF];
+    uint32_t woff[NF];
 #pragma unroll
-    for (int a = 0; a < NF; ++a) wr[a] = laundered(wrow[a]);
-    const char *adummy = reinterpret_cast<const char *>(uni64(reinterpret_cast<uint64_t>(abase)));
-    const char *wdummy = reinterpret_cast<const char *>(uni64(reinterpret_cast<uint64_t>(wr[0])));
+    for (int a = 0; a < NF; ++a) {
+      const char *base = reinterpret_cast<const char *>(uni64(reinterpret_cast<uint64_t>(wrow[a])));
+      wrsrc[a] = make_rsrc(base);
+      woff[a] = (uint32_t)(wrow[a] - base);
+    }
+    // (prefetches past the last chunk read the last chunk again: a clamped uniform offset keeps
+    // the address arithmetic free of selects and temporaries, whose registers the compiler
+    // could otherwise not prove free of pending loads, and would drain the pipeline for)
     auto dma = [&](int c, char *buf) {
-      const bool real = c < nch;
+      const uint32_t off = (uint32_t)(min(c, nch - 1) * RB);
       if (NKB >= kWaves || wv < NKB) {
 #pragma unroll
-        for (int s = 0; s < NDMA; ++s)
-          dma16<COH>(real ? asrc[s] + (size_t)c * RB : adummy, buf + (s * kWaves + wv) * 1024);
+        for (int s = 0; s < NDMA; ++s) dma16<COH>(arsrc, aoff[s], off, buf + (s * kWaves + wv) * 1024);
       }
     };
     auto ldw = [&](uint4(&W)[NF][FL], int c) {
-      const bool real = c < nch;
+      const int off = min(c, nch - 1) * (FL * WSTEP);
 #pragma unroll
       for (int f = 0; f < FL; ++f)
 #pragma unroll
         for (int a = 0; a < NF; ++a)
-          W[a][f] = ld_stream16(real ? wr[a] + (size_t)c * (FL * WSTEP) + f * WSTEP : wdummy);
+          W[a][f] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc[a], woff[a], off + f * WSTEP, kCpolNt));
     };
     // small tiles compute every token group (rows past the tile's end repeat its last
     // row, valid data whose results are not stored); large tiles skip absent groups,
@@ -473,55 +504,34 @@ template <int WT, int MG> struct Core {
       asm volatile("" ::: "memory");  // the stage's prefetches are issued before its math
       chunk_mfma<(MG <= 2)>(acc, W, A, sc, c, ngroups, g, j);
     };
-    if constexpr (NBUF == 2) {
-      // one chunk in flight: wait for it, then issue the next one and compute
-      uint4 wA[NF][FL], wB[NF][FL];
-      dma(0, lb.b0);
-      ldw(wA, 0);
-      for (int c = 0;; c += 2) {
-        wait_vm0();
+    // NBUF register/LDS stages, NBUF - 1 chunks in flight: each step waits only for its own
+    // chunk (vmcnt counts this wave's outstanding operations, which complete in issue order,
+    // so at most NBUF - 2 later chunks may remain), refills the stage freed by the previous
+    // step (the barrier also tells every wave that this stage has been read by all of them),
+    // then computes.  The loop body is unrolled over the stages, so every buffer index is a
+    // constant and the weight stages stay in registers.
+    uint4 W[NBUF][NF][FL];
+#pragma unroll
+    for (int st = 0; st < NBUF - 1; ++st) {
+      dma(st, stage_buf(lb, st));
+      ldw(W[st], st);
+    }
+    bool done = false;
+    for (int c = 0;; c += NBUF) {
+#pragma unroll
+      for (int st = 0; st < NBUF; ++st) {
+        wait_vm<(NBUF - 2) * PER_CHUNK>();
         lds_barrier();
-        dma(c + 1, lb.b1);
-        ldw(wB, c + 1);
-        compute(wA, lb.b0, c);
-        if (c + 1 >= nch) break;
-        wait_vm0();
-        lds_barrier();
-        dma(c + 2, lb.b0);
-        ldw(wA, c + 2);
-        compute(wB, lb.b1, c + 1);
-        if (c + 2 >= nch) break;
+        const int nx = (st + NBUF - 1) % NBUF;
+        dma(c + st + NBUF - 1, stage_buf(lb, nx));
+        ldw(W[nx], c + st + NBUF - 1);
+        compute(W[st], stage_buf(lb, st), c + st);
+        if (c + st + 1 >= nch) {
+          done = true;
+          break;
+        }
       }
-    } else {
-      // two chunks in flight: wait only for the oldest one (vmcnt counts this wave's
-      // outstanding operations, which complete in issue order), then refill the buffer
-      // freed by the previous step; the barrier also tells every wave that the buffer about
-      // to be refilled has been read by all of them
-      uint4 w0[NF][FL], w1[NF][FL], w2[NF][FL];
-      dma(0, lb.b0);
-      ldw(w0, 0);
-      dma(1, lb.b1);
-      ldw(w1, 1);
-      for (int c = 0;; c += 3) {
-        wait_vm<PER_CHUNK>();
-        lds_barrier();
-        dma(c + 2, lb.b2);
-        ldw(w2, c + 2);
-        compute(w0, lb.b0, c);
-        if (c + 1 >= nch) break;
-        wait_vm<PER_CHUNK>();
-        lds_barrier();
-        dma(c + 3, lb.b0);
-        ldw(w0, c + 3);
-        compute(w1, lb.b1, c + 1);
-        if (c + 2 >= nch) break;
-        wait_vm<PER_CHUNK>();
-        lds_barrier();
-        dma(c + 4, lb.b1);
-        ldw(w1, c + 4);
-        compute(w2, lb.b2, c + 2);
-        if (c + 3 >= nch) break;
-      }
+      if (done) break;
     }
     wait_vm0();  // the trailing prefetches land before the caller reuses the buffers
   }
@@ -530,7 +540,7 @@ template <int WT, int MG> struct Core {
 // ---------------------------------------------------------------------------------
 // shared memory
 // ---------------------------------------------------------------------------------
-// bytes of each of the three activation staging buffers (separate LDS variables, see Lds3):
+// bytes of each activation staging buffer (separate LDS variables, see Lds3):
 // the expert tile's chunk, or the router tile's on kernels whose router uses the tile core
 template <int WT, int MG> struct ActBuf {
   using RC = Core<(WT == WF32 ? WF32 : WBF16), router_groups(MG)>;
@@ -1757,7 +1767,8 @@ void moe_persistent(KParams P) {
   __shared__ __attribute__((aligned(16))) char act0[ActBuf<WT, MG>::BYTES];
   __shared__ __attribute__((aligned(16))) char act1[ActBuf<WT, MG>::BYTES];
   __shared__ __attribute__((aligned(16))) char act2[ActBuf<WT, MG>::BYTES];
-  const Lds3 lb{act0, act1, act2};
+  __shared__ __attribute__((aligned(16))) char act3[Shape<WT, MG>::NBUF >= 4 ? ActBuf<WT, MG>::BYTES : 16];
+  const Lds3 lb{act0, act1, act2, act3};
   const int tid = threadIdx.x;
   int *ctrl = P.ctrl;
   int *err = ctrl + kSlotInts * C_ERR;
@@ -1832,22 +1843,125 @@ void moe_persistent(KParams P) {
   // (the first ticket is taken after these items, so the first tickets go to workgroups
   // that are free)
   if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Late phase (m-tiles of more than 16 rows, dynamic schedule).  The gate/up and down items
+  // are split over one queue per XCD: the m-tiles u (the shared expert's first, then the
+  // routed ones, in expert order) form contiguous ranges, XCD x holding [x U / 8, (x+1) U / 8)
+  // of the U m-tiles; workgroups start on the queue of the XCD they run on (hardware register
+  // XCC_ID), so the items of one m-tile share their gathered token rows through that XCD's L2.
+  // Within a queue the gate/up items come first, then the down items, each in groups of
+  // group_m m-tiles taken n-tile by n-tile: consecutive items of a group read the same weight
+  // rows when the group's m-tiles belong to one expert (an expert with more rows than an
+  // m-tile), so its weights are fetched from HBM about once per group, as the grouped
+  // ordering of the vLLM config page (section 03, GROUP_SIZE_M) does for one GEMM.  A
+  // workgroup whose queue is empty takes items from the next XCD's queue, and so on, until
+  // every queue is empty; only then does it take combine items (from its early partition's
+  // counter, continuing with the ticket that ended its early items).  Every wait still ends:
+  // a down item waits for gate/up items of its own m-tile, earlier in the same queue; a
+  // combine item starts only after every gate/up and down item has been taken, by running
+  // workgroups, and those wait for nothing later.
+  int stage = 0;   // 0: early tickets; late phase: 1 per-XCD gate/up and down queues, 2 combine
+  int held = 0;    // late phase: the workgroup's current early ticket (combine items)
+  int xcc = 0, xq = -1, lnext = 0;  // late phase: this XCD, queues emptied so far, prefetched ticket
   for (;;) {
     __syncthreads();
-    if (dynamic) {
-      if (tid == 0) sm.bcast[0] = part + nparts * next;
+    // the next item: phase 0 top-k, 1 shared gate/up, 2 scatter, 3 gate/up, 4 down, 5 combine
+    int phase = -1, idx = 0, item = 0;
+    if (stage == 0) {
+      if (dynamic) {
+        if (tid == 0) sm.bcast[0] = part + nparts * next;
+        __syncthreads();
+      }
+      const int ticket = dynamic ? uni(sm.bcast[0]) : (int)blockIdx.x + step * (int)gridDim.x;
+      ++step;
+      // prefetch the next ticket; its value is read at the top of the next iteration
+      if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      item = ticket + n_Z + n_L;  // (counter-clearing and router items are not ticketed)
+      int i = ticket;
+      if (i < n_K) {
+        phase = 0, idx = i;
+      } else if ((i -= n_K) < n_SG) {
+        phase = 1, idx = i;
+      } else if ((i -= n_SG) < n_S) {
+        phase = 2, idx = i;
+      } else {
+        i -= n_S;
+        if (!dyn) break;
+        if (MG > 1 && P.late) {  // (16-row m-tiles never use the late phase)
+          held = ticket;
+          stage = 1;
+          continue;
+        }
+        if (n_mt < 0 && (n_mt = wg_wait_plan(P, sm)) < 0) break;
+        const int n_G = n_mt * P.nt_gu;
+        const int n_D = (n_mt + P.n_shmt) * P.nt_dn;
+        if (i < n_G) phase = 3, idx = i;
+        else if ((i -= n_G) < n_D) phase = 4, idx = i;
+        else if ((i -= n_D) < P.n_comb) phase = 5, idx = i;
+        else break;
+      }
+    } else if (MG > 1 && stage == 1) {
+      if (n_mt < 0 && (n_mt = wg_wait_plan(P, sm)) < 0) break;
+      const int U = P.n_shmt + n_mt;
+      if (xq < 0) {  // first late item of this workgroup: its XCD's queue
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
+        xq = 0;
+        if (tid == 0)
+          lnext = __hip_atomic_fetch_add(ctrl + kSlotInts * (C_LTICKET + (xcc & (kXcds - 1))), 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const int x = (xcc + xq) & (kXcds - 1);
+      const int lo = x * U / kXcds, hi = (x + 1) * U / kXcds, nu = hi - lo;
+      const int nG = nu * P.nt_gu, nGD = nG + nu * P.nt_dn;
+      if (tid == 0) sm.bcast[0] = lnext;
       __syncthreads();
+      int q = uni(sm.bcast[0]);
+      int *lctr = ctrl + kSlotInts * (C_LTICKET + x);
+      if (q >= nGD) {  // this queue is empty: the next XCD's, and after the last, the combine
+        if (++xq == kXcds) {
+          stage = 2;
+        } else if (tid == 0) {
+          lnext = __hip_atomic_fetch_add(ctrl + kSlotInts * (C_LTICKET + ((xcc + xq) & (kXcds - 1))), 1,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        continue;
+      }
+      if (tid == 0) lnext = __hip_atomic_fetch_add(lctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool gu = q < nG;
+      if (!gu) q -= nG;
+      // q -> (m-tile u, n-tile j): groups of group_m m-tiles, n-tile-major inside a group
+      const int ntile = gu ? P.nt_gu : P.nt_dn, per = P.group_m * ntile;
+      const int grp = q / per, r = q - grp * per, u0 = lo + grp * P.group_m, gs = min(P.group_m, hi - u0);
+      const int j = r / gs, u = u0 + (r - j * gs);
+      const int n_early = n_K + n_SG + n_S;
+      if (!gu) {
+        phase = 4, idx = u * P.nt_dn + j;
+        item = n_Z + n_L + n_early + U * P.nt_gu + idx;
+      } else {
+        phase = u < P.n_shmt ? 1 : 3;
+        idx = (u < P.n_shmt ? u : u - P.n_shmt) * P.nt_gu + j;
+        item = n_Z + n_L + n_early + u * P.nt_gu + j;
+      }
+    } else if (MG > 1) {
+      // combine items: this workgroup's early tickets from `held` on, item = ticket - n_early
+      const int n_early = n_K + n_SG + n_S;
+      const int c = held - n_early;
+      if (c >= P.n_comb) break;
+      if (tid == 0) {
+        sm.bcast[0] = part + nparts * next;
+        next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      held = uni(sm.bcast[0]);
+      phase = 5, idx = c;
+      item = n_Z + n_L + n_early + (P.n_shmt + n_mt) * (P.nt_gu + P.nt_dn) + c;
+    } else {
+      break;
     }
-    const int ticket = dynamic ? uni(sm.bcast[0]) : (int)blockIdx.x + step * (int)gridDim.x;
-    ++step;
-    // prefetch the next ticket; its value is read at the top of the next iteration
-    if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t t_start = P.trace ? wall_clock64() : 0;
     if (P.trace && tid == 0) sm.mark[0] = sm.mark[1] = 0;
     int kind = -1;
-    const int item = ticket + n_Z + n_L;  // (counter-clearing and router items are not ticketed)
-    int i = ticket;
-    if (i < n_K) {
+    const int i = idx;
+    if (phase == 0) {
       if (!(P.phases & PH_IDS_GIVEN) && !logits_seen) {
         if (!wg_wait(ctrl + kSlotInts * C_LDONE, n_L, err, sm)) break;
         logits_seen = true;
@@ -1858,7 +1972,7 @@ void moe_persistent(KParams P) {
       }
       topk_item<kMaxRouterSplit(WT == WFP8, MG)>(P, i, sm);
       kind = K_TOPK;
-    } else if ((i -= n_K) < n_SG) {
+    } else if (phase == 1) {
       if (!zero_seen) {
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
@@ -1866,58 +1980,49 @@ void moe_persistent(KParams P) {
       if constexpr (MG == 1) gateup_unit<WT>(P, true, i, sm, 2 * n_SG <= kWaves * (int)gridDim.x);
       else gateup_item<WT, MG>(P, true, i, sm, lb);
       kind = K_SHGU;
-    } else if ((i -= n_SG) < n_S) {
+    } else if (phase == 2) {
       if (n_mt < 0 && (n_mt = wg_wait_plan(P, sm)) < 0) break;
       scatter_item(P, i, sm);
       wg_signal(ctrl + kSlotInts * C_SDONE);
       kind = K_SCATTER;
-    } else {
-      i -= n_S;
-      if (!dyn) break;
-      if (n_mt < 0 && (n_mt = wg_wait_plan(P, sm)) < 0) break;
-      const int n_G = n_mt * P.nt_gu;
-      const int n_D = (n_mt + P.n_shmt) * P.nt_dn;
+    } else if (phase == 3 || phase == 4) {
       // small-tile units: a deep prefetch (8 steps) when the units are too few to keep the
       // memory system busy, else a shallow one (4 steps): with every wave of the grid
       // streaming, more requests in flight only add contention
-      const bool deep = 2 * n_G <= kWaves * (int)gridDim.x;
-      if (i < n_G + n_D) {
-        if (!scat_seen) {
-          if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S, err, sm)) break;
-          scat_seen = true;
-        }
-        if (!zero_seen) {  // the dependency counters must be cleared before they are used
-          if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
-          zero_seen = true;
-        }
-        if (i < n_G) {
-          if constexpr (MG == 1) gateup_unit<WT>(P, false, i, sm, deep);
-          else gateup_item<WT, MG>(P, false, i, sm, lb);
-          kind = K_GU;
-        } else {
-          if constexpr (MG == 1) {
-            if (!down_unit<WT>(P, i - n_G, sm, deep)) break;
-          } else {
-            if (!down_item<WT, MG>(P, i - n_G, sm, lb)) break;
-          }
-          kind = K_DN;
-        }
-      } else if ((i -= n_G + n_D) < P.n_comb) {
-        // the token's rows of Y are final once the down items of their m-tiles are done (the
-        // slot m-tiles come from the scatter; the counters are valid once cleared)
-        if (!comb_scat_seen) {
-          if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S_comb, err, sm)) break;
-          comb_scat_seen = true;
-        }
-        if (!zero_seen) {
-          if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
-          zero_seen = true;
-        }
-        if (!combine_item<WT>(P, i, sm)) break;
-        kind = K_COMB;
-      } else {
-        break;
+      const bool deep = 2 * n_mt * P.nt_gu <= kWaves * (int)gridDim.x;
+      if (!scat_seen) {
+        if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S, err, sm)) break;
+        scat_seen = true;
       }
+      if (!zero_seen) {  // the dependency counters must be cleared before they are used
+        if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
+        zero_seen = true;
+      }
+      if (phase == 3) {
+        if constexpr (MG == 1) gateup_unit<WT>(P, false, i, sm, deep);
+        else gateup_item<WT, MG>(P, false, i, sm, lb);
+        kind = K_GU;
+      } else {
+        if constexpr (MG == 1) {
+          if (!down_unit<WT>(P, i, sm, deep)) break;
+        } else {
+          if (!down_item<WT, MG>(P, i, sm, lb)) break;
+        }
+        kind = K_DN;
+      }
+    } else {
+      // the token's rows of Y are final once the down items of their m-tiles are done (the
+      // slot m-tiles come from the scatter; the counters are valid once cleared)
+      if (!comb_scat_seen) {
+        if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S_comb, err, sm)) break;
+        comb_scat_seen = true;
+      }
+      if (!zero_seen) {
+        if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
+        zero_seen = true;
+      }
+      if (!combine_item<WT>(P, i, sm)) break;
+      kind = K_COMB;
     }
     record(item, kind, t_start);
   }
@@ -1934,6 +2039,7 @@ void moe_persistent(KParams P) {
       for (int s : {C_ZDONE, C_LDONE, C_KDONE, C_SDONE, C_EXIT}) st_coh(ctrl + kSlotInts * s, 0);
       if (P.reset_err) st_coh(err, 0);
       for (int q = 0; q < kTicketParts; ++q) st_coh(ctrl + kSlotInts * (C_PTICKET + q), 0);
+      for (int q = 0; q < kXcds; ++q) st_coh(ctrl + kSlotInts * (C_LTICKET + q), 0);
       for (int c = 0; c < kPlanCopies; ++c) st_coh(ctrl + plan_flag_word(c), 0);
     }
   }
@@ -2110,7 +2216,10 @@ moe_status launch(const Call &c) {
     P.trace_cap = c.opts->trace_bytes / 32;
   }
 
-  const PhaseCounts pc = phase_counts(L, P.phases);
+  P.schedule = c.opts ? c.opts->schedule : 0;
+  P.late = (L.tiles.late && P.schedule == 0 && (P.phases & PH_FFN)) ? 1 : 0;
+  P.group_m = L.tiles.group_m;
+  const PhaseCounts pc = phase_counts(L, P.phases, P.late != 0);
   P.n_Z = pc.z;
   P.n_L = pc.l;
   P.n_K = pc.k;
@@ -2119,7 +2228,8 @@ moe_status launch(const Call &c) {
   P.gd_words = pc.gd_words;
   P.hist_words = pc.hist_words;
   int n_items = pc.z + pc.l + pc.k + pc.sg + pc.s;
-  if (P.phases & PH_FFN) n_items += L.mt_routed_max * (P.nt_gu + P.nt_dn) + P.n_shmt * P.nt_dn + P.n_comb;
+  if (P.phases & PH_FFN)
+    n_items += L.mt_routed_max * (P.nt_gu + P.nt_dn) + P.n_shmt * P.nt_dn + P.n_comb + (P.late ? P.n_shmt * P.nt_gu : 0);
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
@@ -2128,7 +2238,6 @@ moe_status launch(const Call &c) {
   if (st != MOE_OK) return st;
   int grid = cus * occ;
   if (c.opts && c.opts->grid_wgs > 0) grid = c.opts->grid_wgs;
-  P.schedule = c.opts ? c.opts->schedule : 0;
   P.reset_err = c.reset_err;
   // never more workgroups than can be resident at once: the clearing and router items (and,
   // with the static schedule, every item) are bound to workgroups, so every workgroup of the

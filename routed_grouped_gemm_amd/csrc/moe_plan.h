@@ -19,9 +19,11 @@ namespace {
 constexpr int kThreads = 256;          // threads per workgroup (4 wave64)
 constexpr int kWaves = 4;
 constexpr int kSlotInts = 1024;        // control slots sit 4 KB apart (separate HBM channels)
-constexpr int kCtrlSlots = 32;
+constexpr int kCtrlSlots = 48;
 constexpr int kCtrlBytes = kCtrlSlots * kSlotInts * 4;  // control block at the start of the workspace
 constexpr int kTicketParts = 8;        // ticket counters (see C_PTICKET)
+constexpr int kXcds = 8;               // XCDs of the GPU: one late-phase ticket counter each (C_LTICKET)
+constexpr int kGroupM = 4;             // late phase: m-tiles per group of the grouped item order
 constexpr int kMaxE = 1024;
 constexpr int kMaxFp8ScaleBlocks = 128;  // fp8: 128-wide scale blocks along one wave's K range
 constexpr int kMaxK = 256;
@@ -43,11 +45,12 @@ constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroin
 
 // control-block slots (one int32 each, at int index slot * kSlotInts): a poll of one
 // counter never shares a cache line or channel with the ticket counter or another counter.
-// C_PTICKET + p (p < kTicketParts): ticket counter of partition p, see the persistent
-// kernel.  Slots not named here are unused.
+// C_PTICKET + p (p < kTicketParts): ticket counter of partition p; C_LTICKET + x (x < kXcds):
+// late-phase ticket counter of XCD x; see the persistent kernel.  Slots not named here are
+// unused.
 enum CtrlSlot : int {
   C_MAGIC = 0, C_ZDONE = 2, C_LDONE = 3, C_KDONE = 4, C_SDONE = 6, C_EXIT = 8, C_ERR = 10,
-  C_PTICKET = 16, C_PLANB = 24, C_NSLOTS = kCtrlSlots
+  C_PTICKET = 16, C_PLANB = 24, C_LTICKET = 32, C_NSLOTS = kCtrlSlots
 };
 // C_PLANB .. C_PLANB + 7: copies of the plan flag (n_mt + 1 once the plan is published),
 // eight per slot, 512 bytes apart; workgroup b polls copy b % kPlanCopies
@@ -70,6 +73,9 @@ struct Tiles {
   int rt_experts;  //   mg == 1, else 16 * router_groups(mg) x 64 * NF on the expert tile core)
   int rt_split;    // K splits per router tile (1, 2, 4 or 8): with few tiles, each item takes
                    //   one part of K and the top-k items add the partial sums in order
+  int late;        // 1: gate/up and down items come from per-XCD queues in grouped order
+                   //   (m-tiles of more than 16 rows, dynamic schedule), see the kernel
+  int group_m;     // late phase: m-tiles per group (items of a group run n-tile-major)
 };
 
 struct Layout {
@@ -118,6 +124,10 @@ inline moe_status validate_problem(const moe_problem *p) {
   if (p->d % 256 || p->n % 256) return MOE_ERR_UNSUPPORTED;
   if (p->T * (int64_t)p->k >= (int64_t(1) << 31) - 1) return MOE_ERR_UNSUPPORTED;
   if (p->T * (int64_t)(p->d > p->n ? p->d : p->n) >= (int64_t(1) << 40)) return MOE_ERR_UNSUPPORTED;
+  // the tile core addresses activation rows (hidden, H) with 32-bit offsets
+  const int64_t asz = a == MOE_F32 ? 4 : 2, rows_h = p->T * (int64_t)p->k + (int64_t)p->n_shared * p->T;
+  if (p->T * (int64_t)p->d * asz >= (int64_t(1) << 32) || rows_h * (int64_t)p->n * asz >= (int64_t(1) << 32))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -141,6 +151,8 @@ inline Tiles choose_tiles(const moe_problem *p) {
   if (t.tk > kMaxChunkTokens) t.tk = kMaxChunkTokens;
   if (t.tk < 1) t.tk = 1;
   t.ctok = p->T > 1024 ? 4 : 1;
+  t.late = t.mg > 1 ? 1 : 0;
+  t.group_m = kGroupM;
   t.rt_tokens = t.mg == 1 ? 16 : 16 * router_groups(t.mg);
   t.rt_experts = t.mg == 1 ? 16 : router_groups(t.mg) == 1 ? 128 : 256;
   return t;
@@ -227,7 +239,9 @@ inline Layout make_layout(const moe_problem *p) {
   return L;
 }
 
-inline PhaseCounts phase_counts(const Layout &L, int phases) {
+// late: the launch takes its gate/up and down items from the per-XCD queues (Tiles::late and
+// the dynamic schedule)
+inline PhaseCounts phase_counts(const Layout &L, int phases, bool late) {
   PhaseCounts c{};
   const bool ffn = (phases & PH_FFN) != 0, perm = (phases & PH_PERMUTE) != 0;
   const bool many = L.n_kc > 1;  // else the last top-k item plans and scatters by itself
@@ -236,7 +250,8 @@ inline PhaseCounts phase_counts(const Layout &L, int phases) {
   c.z = (int)ceil_div(c.gd_words + c.hist_words, kZeroPerItem);
   c.l = (phases & PH_ROUTE) ? L.n_lt * L.n_le * L.tiles.rt_split : 0;
   c.k = (phases & (PH_ROUTE | PH_PERMUTE)) ? L.n_kt : 0;
-  c.sg = ffn ? L.n_shmt * L.nt_gu : 0;
+  // (with the late phase, the shared expert's gate/up items are late items too)
+  c.sg = (ffn && !late) ? L.n_shmt * L.nt_gu : 0;
   c.s = (perm && many) ? L.n_kc : 0;
   return c;
 }

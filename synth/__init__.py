@@ -56,15 +56,18 @@ ZIPF_BIAS_FILE = os.path.join(_REPO, "tests", "golden", "skewed_router_bias.json
 CONFIGS = {
     "tiny_fp32": dict(seed=1, T=64, T_gen=64, d=256, E=8, k=2, n=512,
                       act="f32", w="f32", shared=0, zipf=False),
-    "decode_bf16": dict(seed=2, T=16, T_gen=4096, d=2048, E=256, k=8, n=512,
+    "decode_bf16": dict(seed=2, T=16, T_gen=32768, d=2048, E=256, k=8, n=512,
                         act="bf16", w="bf16", shared=0, zipf=False),
-    "prefill_bf16": dict(seed=2, T=4096, T_gen=4096, d=2048, E=256, k=8, n=512,
+    "prefill_bf16": dict(seed=2, T=4096, T_gen=32768, d=2048, E=256, k=8, n=512,
                          act="bf16", w="bf16", shared=0, zipf=False),
     "skewed_bf16": dict(seed=4, T=2048, T_gen=2048, d=4096, E=64, k=4, n=1536,
                         act="bf16", w="bf16", shared=0, zipf=True, zipf_s=1.1),
-    "large_fp8": dict(seed=5, T=4096, T_gen=4096, d=7168, E=256, k=8, n=2048,
+    "large_fp8": dict(seed=5, T=4096, T_gen=16384, d=7168, E=256, k=8, n=2048,
                       act="bf16", w="fp8", shared=1, zipf=False),
 }
+# T_gen above a workload's own T serves the compute-bound points of the same shapes (the
+# prefill shape at T = 16384 and 32768, the fp8 shape at T = 16384): a stream's first values
+# do not depend on how many are drawn, so every smaller T gets the same rows as before.
 LARGE_FP8_T = (1, 8, 64, 512, 4096)
 
 

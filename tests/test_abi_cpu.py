@@ -27,7 +27,7 @@ def test_exports_every_header_function(L):
 
 
 def test_version_and_strings(L):
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
     for code, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARGUMENT"), (2, "MOE_ERR_UNSUPPORTED"),
                        (3, "MOE_ERR_WORKSPACE_TOO_SMALL"), (4, "MOE_ERR_HIP"), (5, "MOE_ERR_DEVICE_FAULT")]:
         assert moe.status_string(code) == name
@@ -58,6 +58,11 @@ def ws_size(p):
     (dict(T=16, d=33024, n=512, E=8, k=2, w="fp8"), UNSUPPORTED),
     (dict(T=16, d=2048, n=16640, E=8, k=2, w="fp8"), UNSUPPORTED),
     (dict(T=16, d=33024, n=16640, E=8, k=2, w="bf16"), 0),
+    # activation tensors (hidden, and the T*k + shared rows of the intermediate) stay below 4 GB
+    (dict(T=1 << 19, d=4096, n=512, E=256, k=1), 0),
+    (dict(T=(1 << 19) + 1, d=4096, n=512, E=256, k=1), UNSUPPORTED),
+    (dict(T=131071, d=2048, n=2048, E=256, k=8), 0),
+    (dict(T=131072, d=2048, n=2048, E=256, k=8), UNSUPPORTED),
 ])
 def test_workspace_size_validation(L, kw, code):
     p = moe.problem(**kw)

@@ -417,6 +417,16 @@ def test_generators_deterministic_and_shared():
     assert np.array_equal(synth.make_router(dec), synth.make_router(pre))
 
 
+def test_longer_token_draws_extend_shorter_ones():
+    """Workloads draw T_gen rows and take the first T: the rows of a T do not depend on T_gen."""
+    a = synth.normal_f32(2, synth.TAG_HIDDEN, 0, (4096, 64), 1.0)
+    b = synth.normal_f32(2, synth.TAG_HIDDEN, 0, (32768, 64), 1.0)
+    assert np.array_equal(a, b[:4096])
+    pre = synth.config("prefill_bf16")
+    big = synth.config("prefill_bf16", 32768)
+    assert np.array_equal(synth.make_hidden(pre), synth.make_hidden(big)[:4096])
+
+
 def test_bf16_encoder_matches_torch():
     x = synth.normal_f32(4, 0, 0, (4096,), 3.0)
     ours = synth.f32_to_bf16_bits(x)

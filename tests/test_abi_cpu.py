@@ -59,8 +59,8 @@ def ws_size(p):
     (dict(T=16, d=2048, n=16640, E=8, k=2, w="fp8"), UNSUPPORTED),
     (dict(T=16, d=33024, n=16640, E=8, k=2, w="bf16"), 0),
     # activation tensors (hidden, and the T*k + shared rows of the intermediate) stay below 4 GB
-    (dict(T=1 << 19, d=4096, n=512, E=256, k=1), 0),
-    (dict(T=(1 << 19) + 1, d=4096, n=512, E=256, k=1), UNSUPPORTED),
+    (dict(T=(1 << 19) - 1, d=4096, n=512, E=256, k=1), 0),
+    (dict(T=1 << 19, d=4096, n=512, E=256, k=1), UNSUPPORTED),
     (dict(T=131071, d=2048, n=2048, E=256, k=8), 0),
     (dict(T=131072, d=2048, n=2048, E=256, k=8), UNSUPPORTED),
 ])

@@ -143,6 +143,7 @@ typedef struct {
 /* (host) optional launch controls, for tests and ablations; pass NULL for the defaults.
  * grid_wgs: workgroups of the persistent launch (0 = CUs x occupancy; larger values are
  *           reduced to CUs x occupancy, since some work items are bound to workgroups).
+ * m_tile_rows, group_m: overrides of the tile table (for the tuner and ablations).
  * trace/trace_bytes: optional device buffer of 32-byte records, one per work item, indexed
  *           by item (clearing, router, then ticketed items in phase order): {start, end}
  *           of the 100 MHz device clock (uint64 each), then the item in bits 0-31 with the
@@ -161,7 +162,12 @@ typedef struct {
   int32_t schedule;
   void *trace;
   int64_t trace_bytes;
-  int32_t reserved[4];
+  int32_t m_tile_rows;  /* 0 = the tuned M-bucket table's; else 16, 32, 64, 128 or 160 (not 160
+                           with fp8 weights).  The workspace must be sized for the chosen tile:
+                           moe_workspace_size reports the table's (a smaller tile needs a few
+                           KB more for its m-tile descriptors), else MOE_ERR_WORKSPACE_TOO_SMALL */
+  int32_t group_m;      /* 0 = the table's; else 1..64 m-tiles per group of the grouped order */
+  int32_t reserved[2];  /* zero */
 } moe_launch_options;
 
 /* (host) the work decomposition moe_forward chooses for a problem (moe_plan_describe). */
@@ -171,7 +177,8 @@ typedef struct {
   int32_t down_cols;       /* output columns per down work item                              */
   int32_t router_k_split;  /* parts the router's K is split into (partial logits added in order) */
   int32_t max_m_tiles;     /* bound on routed m-tiles for any routing (sizes the workspace)   */
-  int32_t reserved[3];
+  int32_t group_m;         /* m-tiles per group of the grouped item order (m-tiles > 16 rows) */
+  int32_t reserved[2];
 } moe_plan_info;
 
 /* The tiling moe_forward uses for p (host only, no HIP call), chosen from the per-M bucket

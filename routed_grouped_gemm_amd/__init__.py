@@ -64,13 +64,14 @@ class RouteOut(ctypes.Structure):
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("m_tile_rows", ctypes.c_int32), ("gateup_cols", ctypes.c_int32), ("down_cols", ctypes.c_int32),
-                ("router_k_split", ctypes.c_int32), ("max_m_tiles", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 3)]
+                ("router_k_split", ctypes.c_int32), ("max_m_tiles", ctypes.c_int32), ("group_m", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class LaunchOptions(ctypes.Structure):
     _fields_ = [("grid_wgs", ctypes.c_int32), ("schedule", ctypes.c_int32), ("trace", ctypes.c_void_p),
-                ("trace_bytes", ctypes.c_int64), ("reserved", ctypes.c_int32 * 4)]
+                ("trace_bytes", ctypes.c_int64), ("m_tile_rows", ctypes.c_int32), ("group_m", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 _lib = None
@@ -256,11 +257,11 @@ def make_weights(weights: dict) -> Weights:
 
 
 def forward(p: Problem, hidden, w_router, bias, weights, ws, out=None, route_out=False, grid_wgs=0,
-            schedule=0, trace=None):
+            schedule=0, trace=None, m_tile_rows=0, group_m=0):
     """The whole layer.  weights: dict with w_gate, w_up, w_down (+ s_*, sh_*) device tensors,
     or a prebuilt Weights struct.  trace: optional device tensor receiving one 32-byte record
-    per work item (see moe_launch_options in include/moe.h).  Returns out, or (out, dict of
-    routing tensors)."""
+    per work item; m_tile_rows, group_m: overrides of the tile table (see moe_launch_options
+    in include/moe.h).  Returns out, or (out, dict of routing tensors)."""
     dev = hidden.device
     T, k, E, d = p.T, p.k, p.E, p.d
     if out is None:
@@ -282,9 +283,10 @@ def forward(p: Problem, hidden, w_router, bias, weights, ws, out=None, route_out
         ro = RouteOut(*[_ptr(rdict[f[0]]) for f in RouteOut._fields_])
     wp, wb = _ws(ws)
     L = _load()
-    if grid_wgs or schedule or trace is not None:
+    if grid_wgs or schedule or trace is not None or m_tile_rows or group_m:
         opts = LaunchOptions(int(grid_wgs), int(schedule), _ptr(trace),
-                             0 if trace is None else trace.numel() * trace.element_size())
+                             0 if trace is None else trace.numel() * trace.element_size(), int(m_tile_rows),
+                             int(group_m))
         code = L.moe_forward_ex(ctypes.byref(p), _ptr(hidden), _ptr(w_router), _ptr(bias), ctypes.byref(W),
                                 _ptr(out), ctypes.byref(ro) if ro is not None else None, wp, wb, _stream(),
                                 ctypes.byref(opts))

@@ -24,6 +24,7 @@ moe_status moe_plan_describe(const moe_problem *p, moe_plan_info *info) {
   info->down_cols = L.tiles.dn_cols;
   info->router_k_split = L.tiles.rt_split;
   info->max_m_tiles = L.mt_routed_max;
+  info->group_m = L.tiles.group_m;
   return MOE_OK;
 }
 

@@ -2141,13 +2141,19 @@ moe_status launch(const Call &c) {
   moe_status st = validate_problem(p);
   if (st != MOE_OK) return st;
   if (!c.ws || (reinterpret_cast<uintptr_t>(c.ws) & 255u)) return MOE_ERR_INVALID_ARGUMENT;
-  const Layout L = make_layout(p);
-  if (c.ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  Tiles forced;
+  bool have_forced = false;
   if (c.opts) {
     if (c.opts->schedule == 2) return MOE_ERR_UNSUPPORTED;
     if (c.opts->grid_wgs < 0 || c.opts->schedule < 0 || c.opts->schedule > 1) return MOE_ERR_INVALID_ARGUMENT;
     if (c.opts->trace_bytes < 0 || (c.opts->trace && !aligned16(c.opts->trace))) return MOE_ERR_INVALID_ARGUMENT;
+    if (c.opts->m_tile_rows || c.opts->group_m) {
+      if (!override_tiles(p, c.opts->m_tile_rows, c.opts->group_m, &forced)) return MOE_ERR_INVALID_ARGUMENT;
+      have_forced = true;
+    }
   }
+  const Layout L = make_layout(p, have_forced ? &forced : nullptr);
+  if (c.ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (p->T == 0) return MOE_OK;
 
   char *ws = static_cast<char *>(c.ws);

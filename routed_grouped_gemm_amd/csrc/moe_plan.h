@@ -10,6 +10,7 @@
 #include <stdint.h>
 
 #include "moe.h"
+#include "moe_tuned.h"
 
 namespace moe {
 // internal linkage: every translation unit that includes this header gets its own copy, so
@@ -131,16 +132,10 @@ inline moe_status validate_problem(const moe_problem *p) {
   return MOE_OK;
 }
 
-inline Tiles choose_tiles(const moe_problem *p) {
+// the tile of a given m-tile size (mg 16-row groups) and late-phase group size
+inline Tiles tiles_for(const moe_problem *p, int mg, int group_m) {
   Tiles t;
-  const double mean_rows = p->E > 0 ? double(p->T) * p->k / p->E : 0.0;
-  // the row count of an expert spreads around the mean by about its square root: pick the
-  // tile so that most experts fit in one m-tile (each extra m-tile re-reads the weights)
-  // (160-row m-tiles past a mean of 100 rows: at a mean of 128 a 128-row tile leaves half
-  // of the experts a second, nearly empty m-tile that re-reads all of their weights; the
-  // fp8 kernels have no registers left for them)
-  t.mg = mean_rows <= 8 ? 1 : mean_rows <= 20 ? 2 : mean_rows <= 44 ? 4
-       : (mean_rows <= 100 || p->w_dtype == MOE_FP8_E4M3) ? 8 : 10;
+  t.mg = mg;
   t.bm = 16 * t.mg;
   t.nf = t.mg == 1 ? 2 : 4;
   // mg == 1: small units streamed by single waves (gate/up: 16 columns, the waves split
@@ -152,10 +147,40 @@ inline Tiles choose_tiles(const moe_problem *p) {
   if (t.tk < 1) t.tk = 1;
   t.ctok = p->T > 1024 ? 4 : 1;
   t.late = t.mg > 1 ? 1 : 0;
-  t.group_m = kGroupM;
+  t.group_m = group_m;
   t.rt_tokens = t.mg == 1 ? 16 : 16 * router_groups(t.mg);
   t.rt_experts = t.mg == 1 ? 16 : router_groups(t.mg) == 1 ? 128 : 256;
   return t;
+}
+
+// The tile from the M-bucket table (moe_tuned.h), keyed by the mean rows per routed expert.
+// The row count of an expert spreads around the mean by about its square root, so a bucket's
+// m-tile is chosen for most experts to fit in one m-tile (each extra m-tile re-reads the
+// expert's weights); the fp8 kernels stop at 128 rows.
+inline Tiles choose_tiles(const moe_problem *p) {
+  const double mean_rows = p->E > 0 ? double(p->T) * p->k / p->E : 0.0;
+  const int wd = p->w_dtype == MOE_F32 ? 0 : p->w_dtype == MOE_BF16 ? 1 : 2;
+  const TileRule *rule = &kTileRules[wd][kNumTileRules - 1];
+  for (int i = 0; i < kNumTileRules; ++i)
+    if (mean_rows <= kTileRules[wd][i].max_mean_rows) {
+      rule = &kTileRules[wd][i];
+      break;
+    }
+  return tiles_for(p, rule->m_tile_rows / 16, rule->group_m);
+}
+
+// An m-tile size and group size given by the caller (0: the table's); false if not valid
+inline bool override_tiles(const moe_problem *p, int m_tile_rows, int group_m, Tiles *t) {
+  *t = choose_tiles(p);
+  if (group_m < 0 || group_m > 64) return false;
+  if (m_tile_rows != 0) {
+    const int r = m_tile_rows;
+    if (r != 16 && r != 32 && r != 64 && r != 128 && r != 160) return false;
+    if (r == 160 && p->w_dtype == MOE_FP8_E4M3) return false;
+    *t = tiles_for(p, r / 16, t->group_m);
+  }
+  if (group_m != 0) t->group_m = group_m;
+  return true;
 }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -172,9 +197,9 @@ struct PhaseCounts {
   int z, l, k, sg, s;
 };
 
-inline Layout make_layout(const moe_problem *p) {
+inline Layout make_layout(const moe_problem *p, const Tiles *forced = nullptr) {
   Layout L{};
-  L.tiles = choose_tiles(p);
+  L.tiles = forced ? *forced : choose_tiles(p);
   const int64_t T = p->T, k = p->k, E = p->E, bm = L.tiles.bm;
   L.T = T;
   L.E = (int)E;

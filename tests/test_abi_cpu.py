@@ -92,6 +92,36 @@ def test_plan_describe_reports_the_m_tile(L, kw, rows):
     assert info["max_m_tiles"] >= min(T * k, E)
 
 
+def test_tile_overrides_are_validated(L):
+    """m_tile_rows / group_m overrides: invalid values are refused before any launch."""
+    VP = ctypes.c_void_p
+    p = moe.problem(16, 2048, 512, 256, 8, layout="packed")
+    W = moe.Weights(*([1 << 21] * 3 + [None] * 9))
+    for rows, gm, want in ((48, 0, INVALID), (0, -1, INVALID), (0, 65, INVALID)):
+        o = moe.LaunchOptions(0, 0, None, 0, rows, gm)
+        assert L.moe_forward_ex(ctypes.byref(p), VP(1 << 20), VP(1 << 20), None, ctypes.byref(W), VP(3 << 20), None,
+                                VP(1 << 24), 1 << 30, None, ctypes.byref(o)) == want
+    pf = moe.problem(16, 2048, 512, 256, 8, w="fp8", layout="packed")
+    Wf = moe.Weights(*([1 << 21] * 6 + [None] * 6))
+    o = moe.LaunchOptions(0, 0, None, 0, 160, 0)   # no 160-row fp8 kernel
+    assert L.moe_forward_ex(ctypes.byref(pf), VP(1 << 20), VP(1 << 20), None, ctypes.byref(Wf), VP(3 << 20), None,
+                            VP(1 << 24), 1 << 30, None, ctypes.byref(o)) == INVALID
+
+
+def test_tile_table_is_well_formed(L):
+    """The compiled-in tile table: mean-row bounds increase, tiles are valid for the dtype, and the
+    chosen tile grows with the mean rows per expert."""
+    for w in ("f32", "bf16", "fp8"):
+        act = "f32" if w == "f32" else "bf16"
+        prev = 0
+        for T in (1, 16, 64, 256, 1024, 4096, 16384, 65536):
+            info = moe.plan_describe(moe.problem(T, 2048, 512, 256, 8, act=act, w=w))
+            assert info["m_tile_rows"] in ((16, 32, 64, 128) if w == "fp8" else (16, 32, 64, 128, 160))
+            assert 1 <= info["group_m"] <= 64
+            assert info["m_tile_rows"] >= prev
+            prev = info["m_tile_rows"]
+
+
 def test_plan_describe_validates(L):
     bad = moe.problem(16, 2000, 512, 256, 8)
     with pytest.raises(moe.MoEError) as ei:

@@ -11,7 +11,8 @@ Every function is pinned by CPU tests against something other than itself
 See moe.py for the passages each step follows.
 """
 from .moe import (  # noqa: F401
-    widen, e4m3_decode, dequant_blocks, router_logits, select_topk, gate_weights,
+    widen, e4m3_decode, dequant_blocks, e4m3_round, fp8_block_scale_exponents, fp8_quantize_rows,
+    router_logits, select_topk, gate_weights,
     route, permute, silu, expert_ffn, combine, moe_forward, moe_forward_view,
     moe_forward_tokens,
     InputsView, rel_frobenius, near_tie_tokens,

@@ -32,7 +32,10 @@ the design notes of the repository):
   * SwiGLU is silu(x Wg^T) * (x Wu^T), then times Wd^T, with no biases;
   * the shared expert has weight 1 and is added after the k routed slots;
   * fp8 weights are OCP E4M3 codes times one float32 scale per 128x128 block;
-  * the permutation is the stable order of (expert, token, slot).
+  * the permutation is the stable order of (expert, token, slot);
+  * in the fp8-activation mode, a GEMM's activations are E4M3 codes times one
+    power-of-two scale per token and 128-element K block, the smallest such
+    scale that fits the block, codes rounded to nearest even (fp8_quantize_rows).
 
 Layouts follow the synthetic-input module: w_router [E,d], w_gate/w_up [E,n,d],
 w_down [E,d,n] (each row is one output channel).
@@ -85,6 +88,67 @@ def dequant_blocks(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> n
     assert s.shape == (R // block, C // block) and R % block == 0 and C % block == 0
     w = w.reshape(R // block, block, C // block, block) * s[:, None, :, None]
     return w.reshape(R, C)
+
+
+# ----------------------------------------------------------------------------
+# fp8 activations (the optional fp8-activation mode of the expert GEMMs)
+# ----------------------------------------------------------------------------
+E4M3_MAX = 448.0  # largest finite OCP E4M3 value: 2^8 * 1.75
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest OCP E4M3 value, ties to the even code.
+
+    Needs |v| <= 448 (the callers scale into that range, so no value saturates).
+    A value in the binade [2^e, 2^(e+1)) has 3 fraction bits, so the E4M3 values
+    there are 2^(e-3) apart; below 2^-6 (the subnormal range) they are 2^-9
+    apart.  Rounding to the nearest multiple of that step, with halves going to
+    the even multiple (numpy's rint), is round-to-nearest-even on the code; the
+    sign is kept, also when the magnitude rounds to zero.
+    """
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("e4m3_round: |v| > 448")
+    _, ex = np.frexp(a)                       # a = m * 2^ex with m in [0.5, 1): binade ex - 1
+    step = np.ldexp(1.0, np.maximum(ex - 1, -6) - 3)
+    return np.copysign(np.rint(a / step) * step, v)
+
+
+def fp8_block_scale_exponents(amax: np.ndarray) -> np.ndarray:
+    """Per block: the smallest integer kexp with amax <= 448 * 2^kexp, at least -127.
+
+    The scale of a block is the power of two 2^kexp (an 8-bit shared exponent, as
+    in the MX formats of [GC-MoE], "two MMA implementations"), the smallest one
+    that maps the block into the E4M3 range.  An all-zero block gets -127.
+    """
+    amax = np.asarray(amax, np.float64)
+    pos = amax > 0
+    safe = np.where(pos, amax, 1.0)
+    kexp = np.ceil(np.log2(safe / E4M3_MAX))
+    # the log is rounded: settle the boundary with exact comparisons
+    kexp = np.where(safe > np.ldexp(E4M3_MAX, kexp.astype(np.int64)), kexp + 1, kexp)
+    kexp = np.where(safe <= np.ldexp(E4M3_MAX, (kexp - 1).astype(np.int64)), kexp - 1, kexp)
+    return np.maximum(np.where(pos, kexp, -127), -127).astype(np.int64)
+
+
+def fp8_quantize_rows(v: np.ndarray, block: int = 128):
+    """Activations as the expert GEMMs read them in the fp8-activation mode.
+
+    Each row (one token) is cut into blocks of `block` consecutive K elements
+    (the 128-wide K block of the fp8_w8a8 block_shape [128,128] of
+    [vLLM-config] section 03); a block is scaled by 2^-kexp
+    (fp8_block_scale_exponents of its largest magnitude), rounded to E4M3 and
+    scaled back.  Returns (the float64 values the GEMM multiplies, kexp [rows,
+    blocks]).
+    """
+    v = np.asarray(v, np.float64)
+    R, C = v.shape
+    assert C % block == 0
+    b = v.reshape(R, C // block, block)
+    kexp = fp8_block_scale_exponents(np.abs(b).max(axis=2) if C else np.zeros((R, 0)))
+    sc = np.ldexp(1.0, kexp)[:, :, None]
+    return (e4m3_round(b / sc) * sc).reshape(R, C), kexp
 
 
 # ----------------------------------------------------------------------------
@@ -178,17 +242,27 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(xr: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+def expert_ffn(xr: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
+               act_quant: bool = False) -> np.ndarray:
     """y = (silu(x Wg^T) * (x Wu^T)) Wd^T for rows x.
 
     [vLLM-config] section 02: each chosen expert is a small FFN of three
     matmuls (gate, up, down) and SwiGLU; [Fusion] section 二: two linear layers
-    and the SwiGLU activation.  No intermediate rounding.
+    and the SwiGLU activation.  No intermediate rounding, except in the
+    fp8-activation mode (act_quant): the gate/up GEMMs read x, and the down GEMM
+    reads h = silu(g) * u, as fp8_quantize_rows makes them (the w8a8 kernel of
+    [vLLM-config] section 03; the requantisation fused after SwiGLU of [GC-MoE],
+    "two MMA implementations").
     """
     xr = np.asarray(xr, np.float64)
+    if act_quant:
+        xr = fp8_quantize_rows(xr)[0]
     g = xr @ np.asarray(wg, np.float64).T
     u = xr @ np.asarray(wu, np.float64).T
-    return (silu(g) * u) @ np.asarray(wd, np.float64).T
+    h = silu(g) * u
+    if act_quant:
+        h = fp8_quantize_rows(h)[0]
+    return h @ np.asarray(wd, np.float64).T
 
 
 def combine(w: np.ndarray, y_slots: np.ndarray, y_shared=None) -> np.ndarray:
@@ -241,11 +315,12 @@ class InputsView:
         return self.inp.sh_gate is not None
 
 
-def moe_forward(x, w_router, bias, k, expert, n_experts, shared=None):
+def moe_forward(x, w_router, bias, k, expert, n_experts, shared=None, act_quant=False):
     """The whole layer: route, permute, per-expert FFN on its group, combine.
 
     expert(e) -> (wg [n,d], wu [n,d], wd [d,n]) float64; shared() likewise or
-    None.  Returns (out [T,d], dict of routing results).
+    None; act_quant: the expert FFNs' fp8-activation mode (expert_ffn).
+    Returns (out [T,d], dict of routing results).
     """
     x = np.asarray(x, np.float64)
     T, d = x.shape
@@ -258,23 +333,23 @@ def moe_forward(x, w_router, bias, k, expert, n_experts, shared=None):
             continue
         tok = perm[lo:hi] // k
         wg, wu, wd = expert(e)
-        y_sorted[lo:hi] = expert_ffn(x[tok], wg, wu, wd)
+        y_sorted[lo:hi] = expert_ffn(x[tok], wg, wu, wd, act_quant)
     y_slots = y_sorted[inv_perm].reshape(T, k, d)
     y_sh = None
     if shared is not None:
         wg, wu, wd = shared()
-        y_sh = expert_ffn(x, wg, wu, wd)
+        y_sh = expert_ffn(x, wg, wu, wd, act_quant)
     out = combine(w, y_slots, y_sh)
     return out, dict(logits=L, ids=ids, weights=w, counts=counts, offsets=offsets,
                      perm=perm, inv_perm=inv_perm)
 
 
-def moe_forward_view(v: InputsView):
+def moe_forward_view(v: InputsView, act_quant=False):
     return moe_forward(v.x, v.w_router, v.bias, v.k, v.expert, v.E,
-                       (lambda: v.expert(v.E)) if v.has_shared else None)
+                       (lambda: v.expert(v.E)) if v.has_shared else None, act_quant)
 
 
-def moe_forward_tokens(v: InputsView, tokens, ids=None, weights=None):
+def moe_forward_tokens(v: InputsView, tokens, ids=None, weights=None, act_quant=False):
     """Outputs of a subset of tokens only (a token's output depends on no other
     token).  ids/weights may be given to use a fixed routing; otherwise the
     oracle's own routing of those tokens is used.  Returns (out [len,d], ids, w).
@@ -291,10 +366,10 @@ def moe_forward_tokens(v: InputsView, tokens, ids=None, weights=None):
             if e not in cache:
                 cache[e] = v.expert(e)
             wg, wu, wd = cache[e]
-            out[r] += weights[r, j] * expert_ffn(xs[r:r + 1], wg, wu, wd)[0]
+            out[r] += weights[r, j] * expert_ffn(xs[r:r + 1], wg, wu, wd, act_quant)[0]
     if v.has_shared:
         wg, wu, wd = v.expert(v.E)
-        out += expert_ffn(xs, wg, wu, wd)
+        out += expert_ffn(xs, wg, wu, wd, act_quant)
     return out, ids, weights
 
 

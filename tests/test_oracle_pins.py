@@ -375,9 +375,138 @@ def check_rel_frobenius():
     return fails
 
 
+# ----------------------------------------------------------------------------
+# fp8 activations: E4M3 rounding, block scales, the quantised FFN
+# ----------------------------------------------------------------------------
+def _e4m3_table():
+    """Every finite non-negative E4M3 value with its code, from the decode definition."""
+    codes = np.arange(0x7f, dtype=np.uint8)  # 0x00 .. 0x7e (0x7f is NaN)
+    return [(float(v), int(c)) for v, c in zip(oracle.e4m3_decode(codes), codes)]
+
+
+def bf_e4m3_round(v):
+    """Nearest E4M3 value by exhaustive search over the code table; a tie goes to the even code."""
+    a = abs(v)
+    best = None
+    for val, code in _e4m3_table():
+        key = (abs(val - a), code & 1)
+        if best is None or key < best[0]:
+            best = (key, val)
+    return math.copysign(best[1], v)
+
+
+def bf_scale_exp(amax):
+    """Smallest integer kexp >= -127 with amax <= 448 * 2^kexp, by counting up."""
+    kexp = -127
+    while amax > 448.0 * 2.0 ** kexp:
+        kexp += 1
+    return kexp
+
+
+def bf_quant_row(row, block=128):
+    out = []
+    for b0 in range(0, len(row), block):
+        blk = row[b0:b0 + block]
+        kexp = bf_scale_exp(max(abs(q) for q in blk))
+        out += [bf_e4m3_round(q / 2.0 ** kexp) * 2.0 ** kexp for q in blk]
+    return out
+
+
+def check_e4m3_round():
+    fails = []
+    table = _e4m3_table()
+    vals = np.array([v for v, _ in table])
+    # every E4M3 value rounds to itself, with either sign
+    for sgn in (1.0, -1.0):
+        if not np.array_equal(oracle.e4m3_round(sgn * vals), sgn * vals):
+            fails.append("e4m3_round moves an E4M3 value")
+    # ties to the even code (closed forms), saturation-free top end, subnormal ties
+    cases = [(1.0625, 1.0), (1.1875, 1.25), (-1.0625, -1.0), (2.0 ** -10, 0.0), (3 * 2.0 ** -10, 2.0 ** -8),
+             (432.0, 448.0), (416.0, 416.0), (448.0, 448.0), (0.3, 0.3125), (17.0, 16.0), (19.0, 20.0)]
+    for v, want in cases:
+        got = float(oracle.e4m3_round(np.array([v]))[0])
+        if got != want:
+            fails.append(f"e4m3_round({v}) = {got}, want {want}")
+    # the torch CPU float8_e4m3fn cast on float32-exact inputs: midpoints between neighbours,
+    # quarter steps either side of them, random values over the whole range
+    pos = vals
+    mids = (pos[:-1] + pos[1:]) / 2
+    quart = np.concatenate([mids - (pos[1:] - pos[:-1]) / 4, mids + (pos[1:] - pos[:-1]) / 4])
+    rng = np.random.default_rng(11)
+    rnd = rng.uniform(-448, 448, 4000) * np.exp2(-rng.integers(0, 14, 4000))
+    probe = np.concatenate([mids, -mids, quart, -quart, rnd]).astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(probe.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    if not np.array_equal(oracle.e4m3_round(probe), ref):
+        fails.append("e4m3_round differs from the torch float8_e4m3fn cast")
+    # brute force on a sample
+    for v in probe[::97]:
+        if float(oracle.e4m3_round(np.array([v]))[0]) != bf_e4m3_round(float(v)):
+            fails.append(f"e4m3_round({v}) differs from exhaustive search")
+            break
+    return fails
+
+
+def check_fp8_quantize_rows():
+    fails = []
+    amax = [448.0, 448.0 * (1 + 2.0 ** -7), 224.0, 224.5, 3.5, 3.5 * (1 + 2.0 ** -7), 1e-3, 0.0, 1e-45, 3e38]
+    got = oracle.fp8_block_scale_exponents(np.array(amax))
+    want = [bf_scale_exp(a) for a in amax]
+    if got.tolist() != want or want[:6] != [0, 1, -1, 0, -7, -6] or want[7] != -127:
+        fails.append(f"block scale exponents {got.tolist()} != {want}")
+    rng = np.random.default_rng(12)
+    # rows with very different block magnitudes, zero blocks, exact E4M3 blocks
+    v = rng.standard_normal((3, 512)) * np.array([1.0, 1e-3, 300.0, 1e4])[None, :].repeat(128, 1)
+    v[1, 128:256] = 0.0
+    v[2, 256:384] = np.array([e for e, _ in _e4m3_table()] + [-448.0]) * 2.0 ** -5
+    q, kexp = oracle.fp8_quantize_rows(v)
+    ref = np.array([bf_quant_row(r) for r in v.tolist()])
+    if not np.array_equal(q, ref):
+        fails.append("fp8_quantize_rows differs from the brute-force quantiser")
+    if not np.array_equal(q[2, 256:384], v[2, 256:384]):
+        fails.append("a block of scaled E4M3 values is not kept exactly")
+    # rows and blocks are quantised independently
+    if not np.array_equal(oracle.fp8_quantize_rows(v[1:2])[0], q[1:2]):
+        fails.append("row quantisation depends on other rows")
+    # error bound: half a step of the value's binade, or of the subnormal range
+    s = np.repeat(np.ldexp(1.0, kexp), 128, axis=1)
+    bound = np.maximum(np.abs(v) * 2.0 ** -4, s * 2.0 ** -10)
+    if np.any(np.abs(q - v) > bound * (1 + 1e-12)):
+        fails.append("fp8 quantisation error above half a step")
+    return fails
+
+
+def check_act_quant_ffn():
+    fails = []
+    rng = np.random.default_rng(13)
+    d, n = 128, 256
+    x = rng.standard_normal((3, d))
+    wg, wu = rng.standard_normal((n, d)) / 11, rng.standard_normal((n, d)) / 11
+    wd = rng.standard_normal((d, n)) / 16
+    got = oracle.expert_ffn(x, wg, wu, wd, act_quant=True)
+    Wg, Wu, Wd = tolist(wg), tolist(wu), tolist(wd)
+    for t in range(3):
+        xq = bf_quant_row(x[t].tolist())
+        h = []
+        for c in range(n):
+            g = math.fsum(xq[i] * Wg[c][i] for i in range(d))
+            u = math.fsum(xq[i] * Wu[c][i] for i in range(d))
+            h.append(g / (1.0 + math.exp(-g)) * u)
+        hq = bf_quant_row(h)
+        ref = [math.fsum(hq[c] * Wd[o][c] for c in range(n)) for o in range(d)]
+        if not np.allclose(got[t], ref, rtol=1e-11, atol=1e-11):
+            fails.append("quantised expert FFN differs from loops")
+            break
+    plain = oracle.expert_ffn(x, wg, wu, wd)
+    rel = np.linalg.norm(got - plain) / np.linalg.norm(plain)
+    if not (1e-3 < rel < 6e-2):
+        fails.append(f"fp8-activation FFN error {rel:.3g} outside the E4M3 error range")
+    return fails
+
+
 ALL_CHECKS = [check_rel_frobenius, check_fp8_decode, check_dequant_blocks, check_widen, check_logits, check_topk_bruteforce,
               check_topk_special, check_weights, check_permute, check_ffn_bruteforce, check_layer_bruteforce,
-              check_closed_forms, check_token_subset]
+              check_closed_forms, check_token_subset, check_e4m3_round, check_fp8_quantize_rows,
+              check_act_quant_ffn]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -509,6 +638,38 @@ def _mut_relfrob_maxabs(got, ref):
     return float(np.abs(got - ref).max() / (den if den > 0 else 1.0))
 
 
+def _mut_e4m3_half_up(v):
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    step = np.ldexp(1.0, np.maximum(ex - 1, -6) - 3)
+    return np.copysign(np.floor(a / step + 0.5) * step, v)
+
+
+def _mut_e4m3_no_subnormal(v):
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    step = np.ldexp(1.0, ex - 1 - 3)
+    return np.copysign(np.rint(a / step) * step, v)
+
+
+def _mut_scale_exp_floor(amax):
+    amax = np.asarray(amax, np.float64)
+    pos = amax > 0
+    k = np.floor(np.log2(np.where(pos, amax, 1.0) / 448.0))
+    return np.maximum(np.where(pos, k, -127), -127).astype(np.int64)
+
+
+def _mut_ffn_h_not_quantised(xr, wg, wu, wd, act_quant=False):
+    xr = np.asarray(xr, np.float64)
+    if act_quant:
+        xr = oracle.moe.fp8_quantize_rows(xr)[0]
+    g = xr @ np.asarray(wg).T
+    u = xr @ np.asarray(wu).T
+    return (g / (1 + np.exp(-g)) * u) @ np.asarray(wd).T
+
+
 _orig_permute = oracle.moe.permute
 
 MUTATIONS = {
@@ -523,6 +684,10 @@ MUTATIONS = {
     "bias_dropped": ("router_logits", _mut_logits_no_bias),
     "rel_frobenius_squared": ("rel_frobenius", _mut_relfrob_squared),
     "rel_frobenius_max_abs": ("rel_frobenius", _mut_relfrob_maxabs),
+    "e4m3_ties_away": ("e4m3_round", _mut_e4m3_half_up),
+    "e4m3_no_subnormals": ("e4m3_round", _mut_e4m3_no_subnormal),
+    "fp8_scale_floor": ("fp8_block_scale_exponents", _mut_scale_exp_floor),
+    "fp8_h_not_requantised": ("expert_ffn", _mut_ffn_h_not_quantised),
 }
 
 

@@ -18,7 +18,8 @@ CPU oracle timed on a bounded sample on this host (cpu_baseline), and a
 `configs` list with the same measurements for the other workloads: prefill (HBM
 and MFMA fractions), the skewed-load layer under the dynamic queue and under the
 static schedule, and the large fp8 layer at T = 1 and 4096.  `--configs` takes a
-comma-separated list of NAME[@T][:static] entries instead.
+comma-separated list of NAME[@T][:static][:fp8act] entries instead (:fp8act: the
+fp8-activation mode of the expert GEMMs, fp8-weight workloads only).
 """
 import os
 
@@ -39,7 +40,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 MALL_BYTES = 256 << 20
-DEFAULT_CONFIGS = "prefill_bf16,skewed_bf16,skewed_bf16:static,large_fp8@1,large_fp8@4096"
+DEFAULT_CONFIGS = "prefill_bf16,skewed_bf16,skewed_bf16:static,large_fp8@1,large_fp8@4096,large_fp8@4096:fp8act"
 
 
 def parse():
@@ -50,7 +51,7 @@ def parse():
     ap.add_argument("--config", default="decode_bf16")
     ap.add_argument("--T", type=int, default=None, help="token count of the headline workload")
     ap.add_argument("--configs", default=DEFAULT_CONFIGS,
-                    help="other workloads for the configs list: NAME[@T][:static],... or 'none'")
+                    help="other workloads for the configs list: NAME[@T][:static][:fp8act],... or 'none'")
     ap.add_argument("--config-steps", type=int, default=30, help="timed steps per entry of the configs list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
@@ -198,7 +199,7 @@ class Workloads:
         return self.dev[key]
 
 
-def measure(wl, name, T, steps, warmup, copies=0, grid=0, schedule=0, want_inputs=False):
+def measure(wl, name, T, steps, warmup, copies=0, grid=0, schedule=0, want_inputs=False, act_quant=False):
     """Times `steps` launches of one workload; returns a dict of its measurements."""
     import numpy as np
     import torch
@@ -209,7 +210,8 @@ def measure(wl, name, T, steps, warmup, copies=0, grid=0, schedule=0, want_input
     key, cfg, inp = wl.inputs(name, T)
     W = wl.device_weights(key, inp)
     p = moe.problem(cfg["T"], cfg["d"], cfg["n"], cfg["E"], cfg["k"], cfg["shared"], cfg["act"], cfg["w"],
-                    layout="packed")
+                    layout="packed", act_quant=act_quant)
+    plan = moe.plan_describe(p)
     x, wr, bias = tensor(inp.hidden), tensor(inp.w_router), tensor(inp.bias)
     ws = moe.alloc_workspace(p)
     # routing of this batch (for the algorithmic byte count) from the library itself
@@ -248,14 +250,17 @@ def measure(wl, name, T, steps, warmup, copies=0, grid=0, schedule=0, want_input
     assert moe.last_device_error(ws) == 0, "device fault flag set during the timed steps"
     per = np.array([s.elapsed_time(e) * 1e3 for s, e in ev])  # us per launch
     avg_us = float(per.mean())
-    mfma = "bf16" if cfg["w"] == "fp8" else cfg["w"]   # fp8 weights are decoded to bf16 for the MFMA
+    # fp8 weights are decoded to bf16 for the MFMA, unless the GEMMs read fp8 activations
+    mfma = ("fp8" if plan["fp8_activations"] else "bf16") if cfg["w"] == "fp8" else cfg["w"]
     peak_mfma = MFMA_PEAK_TFLOPS[mfma]
     gbs = B / (avg_us * 1e-6) / 1e9
     tfl = F / (avg_us * 1e-6) / 1e12
     t_hbm, t_mfma = B / (HBM_PEAK_GBS * 1e9), F / (peak_mfma * 1e12)
-    traffic = measured_traffic(name, None if T is None or name != "large_fp8" else T)
+    wl_name = name + ("_fp8act" if plan["fp8_activations"] else "")
+    traffic = measured_traffic(wl_name, None if T is None or name != "large_fp8" else T)
     res = dict(workload=name, T=cfg["T"], schedule="static" if schedule == 1 else "dynamic",
-               m_tile_rows=moe.plan_describe(p)["m_tile_rows"], experts_touched=touched,
+               fp8_activations=bool(plan["fp8_activations"]),
+               m_tile_rows=plan["m_tile_rows"], experts_touched=touched,
                p50_us=round(float(np.percentile(per, 50)), 2), p99_us=round(float(np.percentile(per, 99)), 2),
                avg_launch_us=round(avg_us, 2), steps=steps, wall_s=wall,
                tokens_per_s=round(cfg["T"] / (avg_us * 1e-6), 1),
@@ -274,10 +279,13 @@ def measure(wl, name, T, steps, warmup, copies=0, grid=0, schedule=0, want_input
 
 
 def parse_entry(e):
-    static = e.endswith(":static")
-    e = e[:-len(":static")] if static else e
-    name, _, t = e.partition("@")
-    return name, (int(t) if t else None), static
+    """NAME[@T][:static][:fp8act] -> (name, T, static, fp8act)"""
+    head, *flags = e.split(":")
+    bad = [f for f in flags if f not in ("static", "fp8act")]
+    if bad:
+        raise SystemExit(f"unknown config flag(s) {bad} in {e!r}")
+    name, _, t = head.partition("@")
+    return name, (int(t) if t else None), "static" in flags, "fp8act" in flags
 
 
 def main():
@@ -329,12 +337,13 @@ def main():
     if a.configs and a.configs != "none":
         entries = []
         for e in a.configs.split(","):
-            name, T, static = parse_entry(e.strip())
-            r = measure(wl, name, T, a.config_steps, 3, schedule=1 if static else 0)
+            name, T, static, fp8act = parse_entry(e.strip())
+            r = measure(wl, name, T, a.config_steps, 3, schedule=1 if static else 0, act_quant=fp8act)
             r.pop("wall_s")
             entries.append(r)
-            print(f"[bench] {name} T={r['T']} {r['schedule']}: {r['avg_launch_us']} us, "
-                  f"hbm {r['hbm_frac']}, mfma {r['mfma_frac']}", file=sys.stderr, flush=True)
+            print(f"[bench] {name} T={r['T']} {r['schedule']}{' fp8act' if r['fp8_activations'] else ''}: "
+                  f"{r['avg_launch_us']} us, hbm {r['hbm_frac']}, mfma {r['mfma_frac']} ({r['mfma_dtype']})",
+                  file=sys.stderr, flush=True)
         res["configs"] = entries
     print(json.dumps(res), flush=True)
 

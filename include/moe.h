@@ -63,7 +63,8 @@
  * compute calls take them packed.  moe_pack_weights is the one conversion, done once at load
  * time; a caller with [E, d, n] gate/up weights transposes them to [E, n, d] first.
  *
- * Supported (act dtype, weight dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ * Supported (act dtype, weight dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3); act_quant
+ * MOE_AQ_FP8 with FP8_E4M3 weights only (else MOE_ERR_UNSUPPORTED).
  * Shape limits: 1 <= k <= E <= 1024, d and n multiples of 256, T*k < 2^31, hidden
  * (T*d) and the expert intermediate (T*k + n_shared*T rows of n) each below 4 GB in the
  * activation dtype; with fp8 weights also d <= 32768 and n <= 16384 (else
@@ -90,7 +91,7 @@ extern "C" {
 
 typedef struct ihipStream_t *hipStream_t;
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -106,6 +107,21 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 /* OCP e4m3fn */ } mo
 
 typedef enum { MOE_W_ROWMAJOR = 0, MOE_W_PACKED = 1 } moe_weight_layout;
 
+/* Activations of the expert GEMMs (moe_problem.act_quant).
+ * MOE_AQ_NONE: the GEMMs read the activations as they are (hidden rows; H rounded to the
+ *   activation dtype), and fp8 weights are decoded exactly to bf16 on the way (w8a16).
+ * MOE_AQ_FP8 (fp8 weights only): the expert GEMMs of m-tiles above 16 rows (moe_plan_info
+ *   m_tile_rows; decode-sized batches use 16-row m-tiles and are unaffected) run on the fp8
+ *   matrix cores with fp8 activations, as the fp8_w8a8 kernel with block_shape [128,128] of
+ *   the vLLM fused-MoE config page (section 03): the gate/up GEMMs read the hidden rows, and
+ *   the down GEMM reads H = silu(g) * u (requantised right after SwiGLU, GC-MoE article, "two
+ *   MMA implementations"), as OCP E4M3 codes with one power-of-two scale per token per 128
+ *   consecutive K elements: 2^s with s the smallest integer (>= -127) such that the block's
+ *   largest magnitude is at most 448 * 2^s, codes rounded to nearest, ties to even.  The
+ *   weights keep their float32 128x128 block scales.  Outputs then carry the E4M3 rounding
+ *   of the activations (about 4% relative error for normally distributed data). */
+typedef enum { MOE_AQ_NONE = 0, MOE_AQ_FP8 = 1 } moe_act_quant;
+
 /* (host) problem descriptor; dtype fields hold moe_dtype values. */
 typedef struct {
   int64_t T;          /* tokens in this call (the M of the grouped GEMM), T >= 0         */
@@ -118,6 +134,7 @@ typedef struct {
   int32_t w_dtype;    /* MOE_F32, MOE_BF16 or MOE_FP8_E4M3: expert weights               */
   int32_t scale_block;/* 128 when w_dtype == MOE_FP8_E4M3, else 0                         */
   int32_t w_layout;   /* moe_weight_layout of w_gate, w_up, w_down and the shared expert     */
+  int32_t act_quant;  /* moe_act_quant: MOE_AQ_NONE, or MOE_AQ_FP8 with fp8 weights           */
 } moe_problem;
 
 /* (host) struct of device pointers to the expert weights (layouts above). */
@@ -150,7 +167,8 @@ typedef struct {
  *           start and end of the item's MFMA tile loop in bits 32-47 and 48-63 (clock ticks
  *           after start; 0 = none), then (workgroup << 32 |
  *           item kind); kinds: 0 clear, 1 router,
- *           2 top-k (+ plan), 3 shared gate/up, 4 scatter, 5 gate/up, 6 down, 7 combine.
+ *           2 top-k (+ plan), 3 shared gate/up, 4 scatter, 5 gate/up, 6 down, 7 combine,
+ *           8 activation quantisation (MOE_AQ_FP8; numbered after the router items).
  *           Items beyond the buffer are not recorded.  NULL (default) records nothing.
  * schedule: 0 = dynamic (work items taken from an atomic queue in the workspace),
  *           1 = static (item i is bound to workgroup i mod grid, like static expert-to-SM
@@ -178,7 +196,9 @@ typedef struct {
   int32_t router_k_split;  /* parts the router's K is split into (partial logits added in order) */
   int32_t max_m_tiles;     /* bound on routed m-tiles for any routing (sizes the workspace)   */
   int32_t group_m;         /* m-tiles per group of the grouped item order (m-tiles > 16 rows) */
-  int32_t reserved[2];
+  int32_t fp8_activations; /* 1: the expert GEMMs read fp8 activations (MOE_AQ_FP8 and m-tiles
+                              above 16 rows), else 0                                         */
+  int32_t reserved;
 } moe_plan_info;
 
 /* The tiling moe_forward uses for p (host only, no HIP call), chosen from the per-M bucket

@@ -31,6 +31,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe.h")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
+AQ_NONE, AQ_FP8 = 0, 1  # moe_act_quant
 _DT = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 ROWMAJOR, PACKED = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
@@ -48,7 +49,8 @@ class MoEError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("n", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("w_dtype", ctypes.c_int32), ("scale_block", ctypes.c_int32), ("w_layout", ctypes.c_int32)]
+                ("w_dtype", ctypes.c_int32), ("scale_block", ctypes.c_int32), ("w_layout", ctypes.c_int32),
+                ("act_quant", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -65,7 +67,7 @@ class RouteOut(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("m_tile_rows", ctypes.c_int32), ("gateup_cols", ctypes.c_int32), ("down_cols", ctypes.c_int32),
                 ("router_k_split", ctypes.c_int32), ("max_m_tiles", ctypes.c_int32), ("group_m", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2)]
+                ("fp8_activations", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class LaunchOptions(ctypes.Structure):
@@ -184,10 +186,12 @@ def status_string(code: int) -> str:
     return _load().moe_status_string(code).decode()
 
 
-def problem(T, d, n, E, k, n_shared=0, act="bf16", w="bf16", layout="rowmajor") -> Problem:
+def problem(T, d, n, E, k, n_shared=0, act="bf16", w="bf16", layout="rowmajor", act_quant=False) -> Problem:
+    """act_quant: the fp8-activation mode of the expert GEMMs (moe_problem.act_quant, fp8
+    weights only)."""
     wd = _DT[w]
     return Problem(int(T), int(d), int(n), int(E), int(k), int(n_shared), _DT[act], wd,
-                   128 if wd == FP8_E4M3 else 0, _LAYOUT[layout])
+                   128 if wd == FP8_E4M3 else 0, _LAYOUT[layout], AQ_FP8 if act_quant else AQ_NONE)
 
 
 def workspace_size(p: Problem) -> int:

@@ -25,6 +25,7 @@ moe_status moe_plan_describe(const moe_problem *p, moe_plan_info *info) {
   info->router_k_split = L.tiles.rt_split;
   info->max_m_tiles = L.mt_routed_max;
   info->group_m = L.tiles.group_m;
+  info->fp8_activations = L.tiles.aq;
   return MOE_OK;
 }
 

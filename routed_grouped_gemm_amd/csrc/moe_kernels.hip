@@ -50,6 +50,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 // 16-byte streaming (nontemporal) load from global memory; the explicit address space keeps
 // it a global_load even when the address comes from a select with a uniform value
@@ -57,7 +58,10 @@ __device__ __forceinline__ uint4 ld_stream16(const void *p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)p));
 }
 
-enum : int { WF32 = 0, WBF16 = 1, WFP8 = 2 };
+// kernel kinds: weight dtype, and for fp8 weights whether the GEMMs read fp8 activations
+// (WQ8: E4M3 activations with power-of-two block scales, fp8 matrix cores; m-tiles > 16 rows)
+enum : int { WF32 = 0, WBF16 = 1, WFP8 = 2, WQ8 = 3 };
+constexpr bool is_fp8w(int wt) { return wt == WFP8 || wt == WQ8; }
 
 constexpr int kCpolNt = 2;  // cache policy of a buffer load: nontemporal (streamed once)
 
@@ -66,6 +70,7 @@ template <int WT> struct Ty;
 template <> struct Ty<WF32> { static constexpr int KU = 16, WSZ = 4, ASZ = 4; };
 template <> struct Ty<WBF16> { static constexpr int KU = 32, WSZ = 2, ASZ = 2; };
 template <> struct Ty<WFP8> { static constexpr int KU = 64, WSZ = 1, ASZ = 2; };
+template <> struct Ty<WQ8> { static constexpr int KU = 64, WSZ = 1, ASZ = 1; };
 
 // per-kernel tile shape: MG 16-token groups per m-tile, NF weight fragments per wave,
 // FL 16-byte weight loads per fragment per K chunk
@@ -95,6 +100,9 @@ struct KParams {
                   //    flag no caller can read)
   int late;       // 1: gate/up and down items from the per-XCD queues, grouped order (see the kernel)
   int group_m;    // late phase: m-tiles per group
+  int aq;         // 1: fp8 activations (Q items quantise the hidden rows; H is requantised)
+  int n_Q;        // activation-quantisation items (bound to workgroups, after the router items)
+  int xs_stride, hs_stride;  // bytes per row of the hidden / H block-scale arrays
   const void *x, *wr;
   const float *bias;
   const void *wg, *wu, *wd;
@@ -114,12 +122,17 @@ struct KParams {
   int *slotmt;    // [T*k] routed m-tile of each (token, slot)
   int4 *desc;
   void *H, *Y;
+  uint8_t *xq;    // fp8 activations: E4M3 codes of the hidden rows [T][d]
+  uint8_t *xs;    // ... their block scales, 2^(xs - 127) per 128-wide block [T][xs_stride]
+  uint8_t *hs;    // ... block scales of H (H itself then holds E4M3 codes) [rows][hs_stride]
   unsigned long long *trace;
   long long trace_cap;
 };
 
 // work item kinds (trace records)
-enum ItemKind : int { K_ZERO = 0, K_ROUTER = 1, K_TOPK = 2, K_SHGU = 3, K_SCATTER = 4, K_GU = 5, K_DN = 6, K_COMB = 7 };
+enum ItemKind : int {
+  K_ZERO = 0, K_ROUTER = 1, K_TOPK = 2, K_SHGU = 3, K_SCATTER = 4, K_GU = 5, K_DN = 6, K_COMB = 7, K_QUANT = 8
+};
 
 // ---------------------------------------------------------------------------------
 // small helpers
@@ -184,6 +197,7 @@ __device__ __forceinline__ void lds_barrier() {
 // not wait for the prefetches before every LDS read.
 struct Lds3 {
   char *b0, *b1, *b2, *b3;  // (b3: four-stage kernels only)
+  uint8_t *sl;              // fp8 activations: block scales of the tile's rows (WQ8 kernels only)
 };
 
 __device__ __forceinline__ char *stage_buf(const Lds3 &lb, int st) {
@@ -208,6 +222,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
 }
 
+// Load through a wave-uniform pointer to data that is read-only for the whole launch (the
+// weight block scales): a scalar load, counted apart from the vector memory operations, so
+// waiting for it never waits for the tile pipeline's prefetches
+__device__ __forceinline__ float ld_uniform(const float *p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) float *>(uni64(reinterpret_cast<uint64_t>(p)));
+}
+
 __device__ __forceinline__ int ld_relaxed(const int *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -229,6 +250,10 @@ __device__ __forceinline__ void st_coh(float *p, float v) {
 }
 __device__ __forceinline__ void st_coh64(void *p, uint64_t v) {
   __hip_atomic_store((gu64 *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+typedef __attribute__((address_space(1))) uint8_t gu8;
+__device__ __forceinline__ void st_coh8(void *p, uint32_t v) {
+  __hip_atomic_store((gu8 *)p, (uint8_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int ld_coh(const int *p) {
   return __hip_atomic_load((const gint *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -340,6 +365,35 @@ __device__ __forceinline__ f4 mfma_step(const uint4 &w, const uint4 &a0, const u
   }
 }
 
+// One fp8 x fp8 MFMA over a 128-wide K block (v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 x
+// E4M3): lane (g, j) gives the 32 codes of weight row j and of token j at the same K
+// positions (its two 16-byte halves: K [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16) of
+// the block), and the token's block scale as an 8-bit exponent (2^(sb - 127)); the weight
+// side's scale is 1 (exponent 127).  Lane (g, j)'s exponent scales 32 of the K terms of
+// token j, and the four lanes of a token hold the same one, so all 128 terms carry it.
+__device__ __forceinline__ f4 mfma_fp8x8(const uint4 &w0, const uint4 &w1, const uint4 &a0, const uint4 &a1, int sb) {
+  const v8i A = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+  const v8i B = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, sb);
+}
+
+// Block scale of fp8 activations: the smallest s >= -127 with amax <= 448 * 2^s, from the bits
+// of amax = (1 + M / 2^23) * 2^(E - 127): 448 * 2^s = 1.75 * 2^(s + 8), so s = E - 135 when
+// M <= 0.75 * 2^23, else E - 134 (exact; zero and subnormal amax give -127)
+__device__ __forceinline__ int fp8_scale_exp(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int s = (int)(u >> 23) - 135 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return s > -127 ? s : -127;
+}
+
+// 4 floats times 2^-s -> 4 E4M3 codes (round to nearest even; |v| * 2^-s <= 448 by the choice
+// of s), packed little-endian
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, int s) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(a, -s), __builtin_ldexpf(b, -s), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(c, -s), __builtin_ldexpf(d, -s), w, true);
+  return (uint32_t)w;
+}
+
 // ---------------------------------------------------------------------------------
 // expert tile core: acc[NF][MG] = W[NF frags of 16 rows, K] . A[MG groups of 16 rows, K]^T
 //
@@ -366,15 +420,49 @@ template <int WT, int MG> struct Core {
   // so LDS reads and MFMAs of different groups interleave freely)
   template <bool FULL>
   __device__ static __forceinline__ void chunk_mfma(f4 (&acc)[NF][MG], const uint4 (&W)[NF][FL], const char *A,
-                                                    const float *const (&sc)[NF], int c, int ngroups, int g, int j) {
-    if constexpr (WT == WFP8) {
+                                                    const float *const (&sc)[NF], int c, int ngroups, int g, int j,
+                                                    const uint8_t *SL, int sstride) {
+    if constexpr (WT == WQ8) {
+      // one 128-wide K block per chunk: per token group, the two 16-byte halves of each row's
+      // codes and the row's block exponent, read from LDS LA groups ahead of their MFMAs; the
+      // block's products are scaled by the weight block scale into the accumulators
+      static_assert(FL == 2, "one scale block per chunk");
+      constexpr int LA = MG < 2 ? MG : 2;
+      struct Bop {
+        uint4 lo, hi;
+        int s;
+      };
+      auto rd = [&](int b) {
+        const int r = b * 16 + j;
+        Bop o;
+        o.lo = *reinterpret_cast<const uint4 *>(A + r * RB + ((g ^ (r & (NCOL - 1))) << 4));
+        o.hi = *reinterpret_cast<const uint4 *>(A + r * RB + (((g + 4) ^ (r & (NCOL - 1))) << 4));
+        o.s = SL[r * sstride + c];
+        return o;
+      };
+      float sw[NF];
+#pragma unroll
+      for (int a = 0; a < NF; ++a) sw[a] = ld_uniform(sc[a] + c);
+      Bop bv[LA];
+#pragma unroll
+      for (int t = 0; t < LA; ++t) bv[t] = rd(t);
+#pragma unroll
+      for (int b = 0; b < MG; ++b) {
+        const Bop cur = bv[b % LA];
+        if (b + LA < MG) bv[b % LA] = rd(b + LA);
+        if (FULL || b == 0 || b < ngroups) {
+#pragma unroll
+          for (int a = 0; a < NF; ++a) acc[a][b] += mfma_fp8x8(W[a][0], W[a][1], cur.lo, cur.hi, cur.s) * sw[a];
+        }
+      }
+    } else if constexpr (WT == WFP8) {
       constexpr int BPC = FL / 2;             // 128-wide scale blocks per chunk
       constexpr int MGC = MG < 4 ? MG : 4;    // token groups per partial-sum pass
 #pragma unroll
       for (int blk = 0; blk < BPC; ++blk) {
         float s[NF];
 #pragma unroll
-        for (int a = 0; a < NF; ++a) s[a] = sc[a][c * BPC + blk];
+        for (int a = 0; a < NF; ++a) s[a] = ld_uniform(sc[a] + c * BPC + blk);
 #pragma unroll
         for (int b0 = 0; b0 < MG; b0 += MGC) {
           if (FULL || b0 == 0 || b0 < ngroups) {
@@ -437,10 +525,12 @@ template <int WT, int MG> struct Core {
   // with the device-coherent policy
   // WSTEP: bytes between consecutive 64-byte K steps of a weight fragment (kWStep for the
   // packed expert weights, 64 for the row-major router rows)
+  // sbase, sstride (fp8 activations only): the rows' block scales, one byte per 128-wide
+  // block, sstride bytes (a multiple of 4) per row; staged in LDS (lb.sl) before the K loop
   template <bool COH, int WSTEP>
   __device__ static void run(f4 (&acc)[NF][MG], const char *const (&wrow)[NF], const float *const (&sc)[NF],
                              const char *abase, size_t arow_bytes, const int *rows, const Lds3 &lb, int K,
-                             int ngroups) {
+                             int ngroups, const uint8_t *sbase = nullptr, int sstride = 0) {
     const int tid = otid(), lane = tid & 63, g = lane >> 4, j = lane & 15;
     const int wv = uni(tid >> 6);
     const int nch = K / KC;
@@ -449,6 +539,19 @@ template <int WT, int MG> struct Core {
 #pragma unroll
       for (int b = 0; b < MG; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
+    if constexpr (WT == WQ8) {
+      // the block scales of the tile's rows, row r at lb.sl + r * sstride: 4 bytes per lane per
+      // load-to-LDS (lanes past the end repeat the last word into the buffer's padding); they
+      // are the oldest loads of the wave, so the K loop's first wait covers them
+      const __amdgpu_buffer_rsrc_t srsrc = make_rsrc(sbase);
+      const int dpr = sstride >> 2, nd = BMR * dpr;
+      for (int w0 = wv * 64; w0 < nd; w0 += kWaves * 64) {
+        const int w = min(w0 + lane, nd - 1), r = w / dpr;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, (__attribute__((address_space(3))) void *)(lb.sl + 4 * w0), 4,
+                                                 (uint32_t)(rows[r] * sstride + 4 * (w - r * dpr)), 0, 0,
+                                                 COH ? kCpolSc1 : 0);
+      }
+    }
     // activation rows: one buffer resource at abase, a per-lane offset per load (the row's
     // 32-bit offset: every activation tensor is below 4 GB) and the chunk offset
     const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(abase);
@@ -502,7 +605,7 @@ template <int WT, int MG> struct Core {
     // which also keeps the compiler from hoisting every LDS read of the chunk at once
     auto compute = [&](const uint4(&W)[NF][FL], const char *A, int c) {
       asm volatile("" ::: "memory");  // the stage's prefetches are issued before its math
-      chunk_mfma<(MG <= 2)>(acc, W, A, sc, c, ngroups, g, j);
+      chunk_mfma<(MG <= 2)>(acc, W, A, sc, c, ngroups, g, j, lb.sl, sstride);
     };
     // NBUF register/LDS stages, NBUF - 1 chunks in flight: each step waits only for its own
     // chunk (vmcnt counts this wave's outstanding operations, which complete in issue order,
@@ -618,6 +721,52 @@ __device__ __forceinline__ void zero_item(const KParams &P, int i) {
     const int idx = lo + q;
     if (idx < P.gd_words) st_coh(P.gudone + idx, 0);
     else if (idx - P.gd_words < P.hist_words) st_coh(P.hist + (idx - P.gd_words), 0);
+  }
+}
+
+// activation quantisation item (fp8 activations): tokens [16 q, 16 q + 16) of the hidden rows
+// -> E4M3 codes in xq and, per 128-wide block, the exponent s (+ 127) of its power-of-two scale
+// in xs (fp8_scale_exp of the block's largest magnitude; codes of v * 2^-s, nearest even).
+// 16 lanes per block (8 values each), 16 blocks per workgroup pass; each lane issues the loads
+// of QB passes before converting any (the rows are read once, so latency is what counts).
+// Lanes past the last block repeat it (same values, so the shuffles see whole blocks) and
+// store nothing.
+constexpr int kQuantBatch = 8;
+__device__ __forceinline__ void quant_item(const KParams &P, int q) {
+  const int tid = otid(), lane = tid & 63, l16 = lane & 15;
+  const int slot = (tid >> 6) * 4 + (lane >> 4);  // this lane group's block within a pass
+  const int nblk = P.d >> 7, t0 = q * kQuantTokens, nt = min(kQuantTokens, P.T - t0), nb = nt * nblk;
+  const uint16_t *x = reinterpret_cast<const uint16_t *>(P.x);
+  for (int base = 0; base < nb; base += 16 * kQuantBatch) {
+    uint4 v[kQuantBatch];
+#pragma unroll
+    for (int u = 0; u < kQuantBatch; ++u) {
+      const int blk = min(base + 16 * u + slot, nb - 1), t = t0 + blk / nblk, kb = blk % nblk;
+      v[u] = ld_glob16(x + (size_t)t * P.d + kb * 128 + 8 * l16);
+    }
+#pragma unroll
+    for (int u = 0; u < kQuantBatch; ++u) {
+      const int blk = base + 16 * u + slot, bc = min(blk, nb - 1), t = t0 + bc / nblk, kb = bc % nblk;
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(w[e] << 16);
+        f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const int se = fp8_scale_exp(mx);
+      if (blk < nb) {
+        const uint64_t codes = (uint64_t)fp8x4(f[0], f[1], f[2], f[3], se) |
+                               ((uint64_t)fp8x4(f[4], f[5], f[6], f[7], se) << 32);
+        st_coh64(P.xq + (size_t)t * P.d + kb * 128 + 8 * l16, codes);
+        if (l16 == 0) st_coh8(P.xs + (size_t)t * P.xs_stride + kb, (uint32_t)(se + 127));
+      }
+    }
   }
 }
 
@@ -1334,7 +1483,7 @@ __device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i
     wrow[a] = frag_ptr(wgb + emat, n0 + 16 * a, (size_t)P.d * wsz, lane);
     wrow[a + NH] = frag_ptr(wub + emat, n0 + 16 * a, (size_t)P.d * wsz, lane);
     sc[a] = sc[a + NH] = nullptr;
-    if constexpr (WT == WFP8) {
+    if constexpr (is_fp8w(WT)) {
       const int nkb = P.d / 128;
       const size_t soff = (shared ? 0 : (size_t)e * (P.n / 128) * nkb) + (size_t)((n0 + 16 * a) / 128) * nkb;
       sc[a] = (shared ? P.shsg : P.sg) + soff;
@@ -1344,19 +1493,64 @@ __device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i
   f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
-  C::template run<false, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows, lb,
-                                 P.d, ngroups);
+  if constexpr (WT == WQ8) {
+    // the hidden rows as E4M3 codes and block scales, written earlier in this launch
+    C::template run<true, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.xq), (size_t)P.d, sm.rows, lb, P.d,
+                                  ngroups, P.xs, P.xs_stride);
+  } else {
+    C::template run<false, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows,
+                                   lb, P.d, ngroups);
+  }
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
+  if constexpr (WT == WQ8) {
+    // H requantised in registers: the item's 128 H columns are one 128-wide block of every
+    // row, so each row's scale is the largest |h| over the four waves (lanes j, j+16, j+32,
+    // j+48 of a wave hold the row's 4 x 8 values; the waves meet in LDS); codes go to H, the
+    // exponent (+ 127) to the row's byte of hs
+    float *red = reinterpret_cast<float *>(&sm.u.red[0][0]);  // [kWaves][BMR]
 #pragma unroll
-  for (int b = 0; b < MG; ++b) {
-    const int r = b * 16 + j;
-    if (r < m) {
+    for (int b = 0; b < MG; ++b) {
+      float mx = 0.f;
 #pragma unroll
-      for (int a = 0; a < NH; ++a) {
-        f4 h;
+      for (int a = 0; a < NH; ++a)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = silu_mul(acc[a][b][q], acc[a + NH][b][q]);
-        store4<WT>(P.H, (hrow0 + r) * (size_t)P.n + n0 + 16 * a + 4 * g, h);
+        for (int q = 0; q < 4; ++q) {
+          acc[a][b][q] = silu_mul(acc[a][b][q], acc[a + NH][b][q]);
+          mx = fmaxf(mx, fabsf(acc[a][b][q]));
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (g == 0) red[wv * C::BMR + b * 16 + j] = mx;
+    }
+    __syncthreads();
+    uint8_t *hq = reinterpret_cast<uint8_t *>(P.H);
+#pragma unroll
+    for (int b = 0; b < MG; ++b) {
+      const int r = b * 16 + j;
+      float amax = red[r];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) amax = fmaxf(amax, red[w * C::BMR + r]);
+      const int se = fp8_scale_exp(amax);
+      if (r < m) {
+#pragma unroll
+        for (int a = 0; a < NH; ++a)
+          st_coh(reinterpret_cast<int *>(hq + (hrow0 + r) * (size_t)P.n + n0 + 16 * a + 4 * g),
+                 (int)fp8x4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3], se));
+        if (wv == 0 && g == 0) st_coh8(P.hs + (hrow0 + r) * (size_t)P.hs_stride + nt, (uint32_t)(se + 127));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < MG; ++b) {
+      const int r = b * 16 + j;
+      if (r < m) {
+#pragma unroll
+        for (int a = 0; a < NH; ++a) {
+          f4 h;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) h[q] = silu_mul(acc[a][b][q], acc[a + NH][b][q]);
+          store4<WT>(P.H, (hrow0 + r) * (size_t)P.n + n0 + 16 * a + 4 * g, h);
+        }
       }
     }
   }
@@ -1397,7 +1591,7 @@ __device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm, const
   for (int a = 0; a < NF; ++a) {
     wrow[a] = frag_ptr(wdb + emat, min(d0 + 16 * a, P.d - 16), (size_t)P.n * wsz, lane);
     sc[a] = nullptr;
-    if constexpr (WT == WFP8) {
+    if constexpr (is_fp8w(WT)) {
       const int nkb = P.n / 128;
       const float *sb = (shared ? P.shsd : P.sd) + (shared ? 0 : (size_t)e * (P.d / 128) * nkb);
       sc[a] = sb + (size_t)(min(d0 + 16 * a, P.d - 1) / 128) * nkb;
@@ -1406,8 +1600,12 @@ __device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm, const
   f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
-  C::template run<true, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n * asz, sm.rows, lb,
-                                P.n, ngroups);
+  if constexpr (WT == WQ8)  // H as E4M3 codes (one byte per value) and block scales
+    C::template run<true, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n, sm.rows, lb, P.n,
+                                  ngroups, P.hs, P.hs_stride);
+  else
+    C::template run<true, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n * asz, sm.rows, lb,
+                                  P.n, ngroups);
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
 #pragma unroll
   for (int b = 0; b < MG; ++b) {
@@ -1759,6 +1957,10 @@ __device__ __forceinline__ bool combine_item(const KParams &P, int c, SM &sm) {
 template <int WT, int MG> struct Occ {
   static constexpr int waves = MG == 1 ? (WT == WFP8 ? 2 : 3) : (MG >= 8 || (MG == 4 && WT != WBF16)) ? 1 : 2;
 };
+// block scales of the tile's rows (WQ8): at most 256 blocks (d <= 32768) per row
+template <int WT, int MG> struct ScaleBuf {
+  static constexpr int BYTES = WT == WQ8 ? MG * 16 * 256 : 16;
+};
 
 template <int WT, int MG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occ<WT, MG>::waves)))
@@ -1768,7 +1970,8 @@ void moe_persistent(KParams P) {
   __shared__ __attribute__((aligned(16))) char act1[ActBuf<WT, MG>::BYTES];
   __shared__ __attribute__((aligned(16))) char act2[ActBuf<WT, MG>::BYTES];
   __shared__ __attribute__((aligned(16))) char act3[Shape<WT, MG>::NBUF >= 4 ? ActBuf<WT, MG>::BYTES : 16];
-  const Lds3 lb{act0, act1, act2, act3};
+  __shared__ __attribute__((aligned(16))) uint8_t scl[ScaleBuf<WT, MG>::BYTES];
+  const Lds3 lb{act0, act1, act2, act3, scl};
   const int tid = threadIdx.x;
   int *ctrl = P.ctrl;
   int *err = ctrl + kSlotInts * C_ERR;
@@ -1779,8 +1982,11 @@ void moe_persistent(KParams P) {
     return;
   }
   const int n_Z = P.n_Z, n_L = P.n_L, n_K = P.n_K, n_SG = P.n_SG, n_S = P.n_S;
+  const int n_Q = WT == WQ8 ? P.n_Q : 0;
+  const int n_bound = n_Z + n_L + n_Q;  // items before the first ticketed one (trace numbering)
   const bool dyn = (P.phases & (PH_FFN | PH_COMBINE)) != 0;
   bool zero_seen = false, logits_seen = false, scat_seen = false, comb_scat_seen = false;
+  bool quant_seen = WT != WQ8;
   // the combine needs the whole scatter: the S items, or the last K item's for one chunk
   const int n_S_comb = n_S + ((P.n_kc <= 1 && (P.phases & PH_PERMUTE)) ? 1 : 0);
   int n_mt = -1;
@@ -1840,6 +2046,20 @@ void moe_persistent(KParams P) {
     wg_signal(ctrl + kSlotInts * C_ZDONE);
     record(z, K_ZERO, t_start);
   }
+  // Activation-quantisation items (fp8 activations) take no ticket either: workgroup b runs
+  // items b - n_L, b - n_L + grid, ... (mod grid: the workgroups after the router items' first
+  // round start on them).  They wait for nothing; the gate/up items wait for all of them.
+  if constexpr (WT == WQ8) {
+    const int G = (int)gridDim.x;
+    for (int q = (((int)blockIdx.x - n_L) % G + G) % G; q < n_Q; q += G) {
+      __syncthreads();
+      const uint64_t t_start = P.trace ? wall_clock64() : 0;
+      if (P.trace && tid == 0) sm.mark[0] = sm.mark[1] = 0;
+      quant_item(P, q);
+      wg_signal(ctrl + kSlotInts * C_QDONE);
+      record(n_Z + n_L + q, K_QUANT, t_start);
+    }
+  }
   // (the first ticket is taken after these items, so the first tickets go to workgroups
   // that are free)
   if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1875,7 +2095,7 @@ void moe_persistent(KParams P) {
       ++step;
       // prefetch the next ticket; its value is read at the top of the next iteration
       if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      item = ticket + n_Z + n_L;  // (counter-clearing and router items are not ticketed)
+      item = ticket + n_bound;  // (counter-clearing, router and quantisation items are not ticketed)
       int i = ticket;
       if (i < n_K) {
         phase = 0, idx = i;
@@ -1935,11 +2155,11 @@ void moe_persistent(KParams P) {
       const int n_early = n_K + n_SG + n_S;
       if (!gu) {
         phase = 4, idx = u * P.nt_dn + j;
-        item = n_Z + n_L + n_early + U * P.nt_gu + idx;
+        item = n_bound + n_early + U * P.nt_gu + idx;
       } else {
         phase = u < P.n_shmt ? 1 : 3;
         idx = (u < P.n_shmt ? u : u - P.n_shmt) * P.nt_gu + j;
-        item = n_Z + n_L + n_early + u * P.nt_gu + j;
+        item = n_bound + n_early + u * P.nt_gu + j;
       }
     } else if (MG > 1) {
       // combine items: this workgroup's early tickets from `held` on, item = ticket - n_early
@@ -1953,7 +2173,7 @@ void moe_persistent(KParams P) {
       __syncthreads();
       held = uni(sm.bcast[0]);
       phase = 5, idx = c;
-      item = n_Z + n_L + n_early + (P.n_shmt + n_mt) * (P.nt_gu + P.nt_dn) + c;
+      item = n_bound + n_early + (P.n_shmt + n_mt) * (P.nt_gu + P.nt_dn) + c;
     } else {
       break;
     }
@@ -1970,12 +2190,16 @@ void moe_persistent(KParams P) {
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
       }
-      topk_item<kMaxRouterSplit(WT == WFP8, MG)>(P, i, sm);
+      topk_item<kMaxRouterSplit(is_fp8w(WT), MG)>(P, i, sm);
       kind = K_TOPK;
     } else if (phase == 1) {
       if (!zero_seen) {
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
+      }
+      if (!quant_seen) {  // the quantised hidden rows
+        if (!wg_wait(ctrl + kSlotInts * C_QDONE, n_Q, err, sm)) break;
+        quant_seen = true;
       }
       if constexpr (MG == 1) gateup_unit<WT>(P, true, i, sm, 2 * n_SG <= kWaves * (int)gridDim.x);
       else gateup_item<WT, MG>(P, true, i, sm, lb);
@@ -1997,6 +2221,10 @@ void moe_persistent(KParams P) {
       if (!zero_seen) {  // the dependency counters must be cleared before they are used
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
+      }
+      if (phase == 3 && !quant_seen) {  // the quantised hidden rows
+        if (!wg_wait(ctrl + kSlotInts * C_QDONE, n_Q, err, sm)) break;
+        quant_seen = true;
       }
       if (phase == 3) {
         if constexpr (MG == 1) gateup_unit<WT>(P, false, i, sm, deep);
@@ -2036,7 +2264,7 @@ void moe_persistent(KParams P) {
     wait_vm0();
     const int old = __hip_atomic_fetch_add(ctrl + kSlotInts * C_EXIT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (int)gridDim.x - 1) {
-      for (int s : {C_ZDONE, C_LDONE, C_KDONE, C_SDONE, C_EXIT}) st_coh(ctrl + kSlotInts * s, 0);
+      for (int s : {C_ZDONE, C_LDONE, C_KDONE, C_SDONE, C_QDONE, C_EXIT}) st_coh(ctrl + kSlotInts * s, 0);
       if (P.reset_err) st_coh(err, 0);
       for (int q = 0; q < kTicketParts; ++q) st_coh(ctrl + kSlotInts * (C_PTICKET + q), 0);
       for (int q = 0; q < kXcds; ++q) st_coh(ctrl + kSlotInts * (C_LTICKET + q), 0);
@@ -2067,34 +2295,46 @@ __global__ void pack_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ d
 typedef void (*KernelFn)(KParams);
 
 template <int WT> KernelFn pick_kernel(int mg) {
-  switch (mg) {
-    case 1: return moe_persistent<WT, 1>;
-    case 2: return moe_persistent<WT, 2>;
-    case 4: return moe_persistent<WT, 4>;
-    default: break;
+  if constexpr (WT == WQ8) {  // (m-tiles above 16 rows only, at most 128 rows)
+    return mg == 2 ? moe_persistent<WQ8, 2> : mg == 4 ? moe_persistent<WQ8, 4> : moe_persistent<WQ8, 8>;
+  } else {
+    switch (mg) {
+      case 1: return moe_persistent<WT, 1>;
+      case 2: return moe_persistent<WT, 2>;
+      case 4: return moe_persistent<WT, 4>;
+      default: break;
+    }
+    if constexpr (WT != WFP8) {  // (no 160-row fp8 kernel: see choose_tiles)
+      if (mg == 10) return moe_persistent<WT, 10>;
+    }
+    return moe_persistent<WT, 8>;
   }
-  if constexpr (WT != WFP8) {  // (no 160-row fp8 kernel: see choose_tiles)
-    if (mg == 10) return moe_persistent<WT, 10>;
-  }
-  return moe_persistent<WT, 8>;
 }
 
-KernelFn kernel_for(int w_dtype, int mg) {
-  if (w_dtype == MOE_F32) return pick_kernel<WF32>(mg);
-  if (w_dtype == MOE_BF16) return pick_kernel<WBF16>(mg);
+// kind: WF32, WBF16, WFP8 or WQ8 (fp8 weights and activations)
+KernelFn kernel_for(int kind, int mg) {
+  if (kind == WF32) return pick_kernel<WF32>(mg);
+  if (kind == WBF16) return pick_kernel<WBF16>(mg);
+  if (kind == WQ8) return pick_kernel<WQ8>(mg);
   return pick_kernel<WFP8>(mg);
+}
+
+int kernel_kind(const moe_problem *p, const Tiles &t) {
+  if (p->w_dtype == MOE_F32) return WF32;
+  if (p->w_dtype == MOE_BF16) return WBF16;
+  return t.aq ? WQ8 : WFP8;
 }
 
 struct DevInfo {
   int cus = 0;
-  int occ[3][5] = {};  // [weight dtype][m-tile size 16, 32, 64, 128, 160 rows]
+  int occ[4][5] = {};  // [kernel kind][m-tile size 16, 32, 64, 128, 160 rows]
 };
 
 std::mutex g_mu;
 DevInfo g_dev[64];
 bool g_have[64];
 
-moe_status device_info(int dev, int w_dtype, int mg, int *cus, int *occ) {
+moe_status device_info(int dev, int kind, int mg, int *cus, int *occ) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (dev < 0 || dev >= 64) return MOE_ERR_HIP;
   DevInfo &D = g_dev[dev];
@@ -2103,10 +2343,10 @@ moe_status device_info(int dev, int w_dtype, int mg, int *cus, int *occ) {
     g_have[dev] = true;
   }
   const int mi = mg == 1 ? 0 : mg == 2 ? 1 : mg == 4 ? 2 : mg == 8 ? 3 : 4;
-  int &o = D.occ[w_dtype][mi];
+  int &o = D.occ[kind][mi];
   if (o == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void *>(kernel_for(w_dtype, mg)),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void *>(kernel_for(kind, mg)),
                                                      kThreads, 0) != hipSuccess)
       return MOE_ERR_HIP;
     o = nb > 0 ? nb : 1;
@@ -2217,6 +2457,12 @@ moe_status launch(const Call &c) {
   P.mtok = reinterpret_cast<int *>(ws + L.off_mtok);
   P.H = ws + L.off_h;
   P.Y = ws + L.off_y;
+  P.aq = L.tiles.aq;
+  P.xq = reinterpret_cast<uint8_t *>(ws + L.off_xq);
+  P.xs = reinterpret_cast<uint8_t *>(ws + L.off_xs);
+  P.hs = reinterpret_cast<uint8_t *>(ws + L.off_hs);
+  P.xs_stride = L.xs_stride;
+  P.hs_stride = L.hs_stride;
   if (c.opts && c.opts->trace) {
     P.trace = static_cast<unsigned long long *>(c.opts->trace);
     P.trace_cap = c.opts->trace_bytes / 32;
@@ -2231,16 +2477,18 @@ moe_status launch(const Call &c) {
   P.n_K = pc.k;
   P.n_SG = pc.sg;
   P.n_S = pc.s;
+  P.n_Q = pc.q;
   P.gd_words = pc.gd_words;
   P.hist_words = pc.hist_words;
-  int n_items = pc.z + pc.l + pc.k + pc.sg + pc.s;
+  int n_items = pc.z + pc.l + pc.q + pc.k + pc.sg + pc.s;
   if (P.phases & PH_FFN)
     n_items += L.mt_routed_max * (P.nt_gu + P.nt_dn) + P.n_shmt * P.nt_dn + P.n_comb + (P.late ? P.n_shmt * P.nt_gu : 0);
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
   int cus = 0, occ = 0;
-  st = device_info(dev, p->w_dtype, L.tiles.mg, &cus, &occ);
+  const int kind = kernel_kind(p, L.tiles);
+  st = device_info(dev, kind, L.tiles.mg, &cus, &occ);
   if (st != MOE_OK) return st;
   int grid = cus * occ;
   if (c.opts && c.opts->grid_wgs > 0) grid = c.opts->grid_wgs;
@@ -2251,7 +2499,7 @@ moe_status launch(const Call &c) {
   if (grid > cus * occ) grid = cus * occ;
   if (grid > n_items && P.schedule == 0) grid = n_items > 0 ? n_items : 1;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kernel_for(p->w_dtype, L.tiles.mg), dim3(grid), dim3(kThreads), 0, c.stream, P);
+  hipLaunchKernelGGL(kernel_for(kind, L.tiles.mg), dim3(grid), dim3(kThreads), 0, c.stream, P);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }

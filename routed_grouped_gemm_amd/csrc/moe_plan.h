@@ -42,6 +42,7 @@ constexpr int kMaxChunkTokens = 128;   // tokens per scatter chunk (rank bitmask
 constexpr int kMaxChunkSlots = 1024;   // (token, slot) pairs per chunk
 constexpr int kCombineUnroll = 2;      // combine: (token, column) pairs per thread in flight
 constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroing item
+constexpr int kQuantTokens = 16;       // tokens per activation-quantisation item (fp8 activations)
 
 
 // control-block slots (one int32 each, at int index slot * kSlotInts): a poll of one
@@ -50,7 +51,7 @@ constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroin
 // late-phase ticket counter of XCD x; see the persistent kernel.  Slots not named here are
 // unused.
 enum CtrlSlot : int {
-  C_MAGIC = 0, C_ZDONE = 2, C_LDONE = 3, C_KDONE = 4, C_SDONE = 6, C_EXIT = 8, C_ERR = 10,
+  C_MAGIC = 0, C_ZDONE = 2, C_LDONE = 3, C_KDONE = 4, C_SDONE = 6, C_EXIT = 8, C_ERR = 10, C_QDONE = 12,
   C_PTICKET = 16, C_PLANB = 24, C_LTICKET = 32, C_NSLOTS = kCtrlSlots
 };
 // C_PLANB .. C_PLANB + 7: copies of the plan flag (n_mt + 1 once the plan is published),
@@ -77,6 +78,7 @@ struct Tiles {
   int late;        // 1: gate/up and down items come from per-XCD queues in grouped order
                    //   (m-tiles of more than 16 rows, dynamic schedule), see the kernel
   int group_m;     // late phase: m-tiles per group (items of a group run n-tile-major)
+  int aq;          // 1: the expert GEMMs read fp8 activations (MOE_AQ_FP8, m-tiles above 16 rows)
 };
 
 struct Layout {
@@ -92,9 +94,10 @@ struct Layout {
   int nt_gu, nt_dn;      // gate/up and down items per m-tile
   int n_comb;            // combine items
   int64_t rows_h;        // rows of H and Y: T*k + n_shared*T
+  int xs_stride, hs_stride;  // fp8 activations: bytes per row of the hidden / H block scales
   // byte offsets into the workspace
   size_t off_gudone, off_desc, off_logits, off_lpart, off_ids, off_wts, off_hist, off_counts, off_offsets, off_mtoff,
-      off_perm, off_invperm, off_mtok, off_slotmt, off_h, off_y, total;
+      off_perm, off_invperm, off_mtok, off_slotmt, off_xq, off_xs, off_hs, off_h, off_y, total;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -121,6 +124,8 @@ inline moe_status validate_problem(const moe_problem *p) {
     return MOE_ERR_INVALID_ARGUMENT;
   }
   if (p->w_layout != MOE_W_ROWMAJOR && p->w_layout != MOE_W_PACKED) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->act_quant != MOE_AQ_NONE && p->act_quant != MOE_AQ_FP8) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->act_quant == MOE_AQ_FP8 && w != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
   if (p->E > kMaxE || p->k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (p->d % 256 || p->n % 256) return MOE_ERR_UNSUPPORTED;
   if (p->T * (int64_t)p->k >= (int64_t(1) << 31) - 1) return MOE_ERR_UNSUPPORTED;
@@ -148,6 +153,7 @@ inline Tiles tiles_for(const moe_problem *p, int mg, int group_m) {
   t.ctok = p->T > 1024 ? 4 : 1;
   t.late = t.mg > 1 ? 1 : 0;
   t.group_m = group_m;
+  t.aq = (p->act_quant == MOE_AQ_FP8 && t.mg > 1) ? 1 : 0;
   t.rt_tokens = t.mg == 1 ? 16 : 16 * router_groups(t.mg);
   t.rt_experts = t.mg == 1 ? 16 : router_groups(t.mg) == 1 ? 128 : 256;
   return t;
@@ -188,13 +194,15 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // words of one per-m-tile counter array (gate/up done, down done), padded to 256 bytes
 inline int ctr_words(const Layout &L) { return (int)align_up((size_t)(L.mt_routed_max + L.n_shmt + 1), 64); }
 
-// Work items of one launch, per phase, in order: Z (clear counters), L (router), K (top-k),
-// SG (shared gate/up), S (scatter); the routed gate/up, down and combine items follow and are
-// counted on the device once the plan exists.  The Z and router items take no ticket (each
-// workgroup runs its share of them first); the others are handed out by ticket in this order.
+// Work items of one launch, per phase, in order: Z (clear counters), L (router), Q (fp8
+// activations: quantise the hidden rows), K (top-k), SG (shared gate/up), S (scatter); the
+// routed gate/up, down and combine items follow and are counted on the device once the plan
+// exists.  The Z, router and Q items take no ticket (each workgroup runs its share of them
+// first); the others are handed out by ticket in this order.
 struct PhaseCounts {
   int gd_words, hist_words;  // words cleared by Z items: dependency counters, chunk histograms
   int z, l, k, sg, s;
+  int q;                     // activation-quantisation items (fp8 activations; bound like Z, L)
 };
 
 inline Layout make_layout(const moe_problem *p, const Tiles *forced = nullptr) {
@@ -234,7 +242,11 @@ inline Layout make_layout(const moe_problem *p, const Tiles *forced = nullptr) {
   L.nt_dn = (int)ceil_div(p->d, L.tiles.dn_cols);
   L.n_comb = (int)ceil_div(T, L.tiles.ctok);
   L.rows_h = tk + (int64_t)p->n_shared * T;
-  const size_t asz = dtype_size(p->act_dtype);
+  // fp8 activations: one scale byte per 128-wide block, rows padded to whole dwords
+  L.xs_stride = (int)align_up((size_t)(p->d / 128), 4);
+  L.hs_stride = (int)align_up((size_t)(p->n / 128), 4);
+  const size_t asz = dtype_size(p->act_dtype), hsz = L.tiles.aq ? 1 : asz;
+  const bool aq = L.tiles.aq != 0;
   size_t o = kCtrlBytes;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -258,7 +270,10 @@ inline Layout make_layout(const moe_problem *p, const Tiles *forced = nullptr) {
   L.off_invperm = take(sizeof(int32_t) * (size_t)tk);
   L.off_mtok = take(sizeof(int32_t) * (bm == 16 ? (size_t)L.mt_routed_max * 16 : 16));
   L.off_slotmt = take(sizeof(int32_t) * (size_t)tk);
-  L.off_h = take(asz * (size_t)L.rows_h * (size_t)p->n);
+  L.off_xq = take(aq ? (size_t)T * (size_t)p->d : 0);
+  L.off_xs = take(aq ? (size_t)T * (size_t)L.xs_stride : 0);
+  L.off_hs = take(aq ? (size_t)L.rows_h * (size_t)L.hs_stride : 0);
+  L.off_h = take(hsz * (size_t)L.rows_h * (size_t)p->n);
   L.off_y = take(asz * (size_t)L.rows_h * (size_t)p->d);
   L.total = o;
   return L;
@@ -278,6 +293,7 @@ inline PhaseCounts phase_counts(const Layout &L, int phases, bool late) {
   // (with the late phase, the shared expert's gate/up items are late items too)
   c.sg = (ffn && !late) ? L.n_shmt * L.nt_gu : 0;
   c.s = (perm && many) ? L.n_kc : 0;
+  c.q = (ffn && L.tiles.aq) ? (int)ceil_div(L.T, kQuantTokens) : 0;
   return c;
 }
 

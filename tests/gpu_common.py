@@ -49,8 +49,8 @@ def require_gpu():
         build.build()
 
 
-def run_forward(inp, layout="packed", **kw):
-    p, x, wr, b, W = to_device(inp, layout=layout)
+def run_forward(inp, layout="packed", act_quant=False, **kw):
+    p, x, wr, b, W = to_device(inp, layout=layout, act_quant=act_quant)
     # a forced m-tile may need a few KB more of m-tile descriptors than the table's tile
     ws = moe.alloc_workspace(p, extra=(4 << 20) if kw.get("m_tile_rows") else 0)
     out, r = moe.forward(p, x, wr, b, W, ws, route_out=True, **kw)
@@ -105,33 +105,116 @@ def compare_outputs(got, ref, tol, what=""):
     return err, worst
 
 
-def oracle_reference(v, L, ids, gids, mism, tokens=None, ref=None):
+def oracle_reference(v, L, ids, gids, mism, tokens=None, ref=None, act_quant=False):
     """Oracle outputs with the oracle's own routing, except near-tie tokens where the
     GPU legitimately chose differently: those use the GPU's ids (weights from the
-    oracle's logits).  ref: the oracle's outputs of these tokens, if already computed."""
+    oracle's logits).  ref: the oracle's outputs of these tokens, if already computed.
+    act_quant: the oracle's fp8-activation mode (the library used fp8 activations)."""
     toks = np.arange(v.x.shape[0]) if tokens is None else np.asarray(tokens)
     if ref is not None:
         ref = np.array(ref, np.float64, copy=True)
     elif tokens is None:
-        ref, _ = oracle.moe_forward_view(v)
+        ref, _ = oracle.moe_forward_view(v, act_quant=act_quant)
     else:
-        ref, _, _ = oracle.moe_forward_tokens(v, toks)
+        ref, _, _ = oracle.moe_forward_tokens(v, toks, act_quant=act_quant)
     for r_i in np.nonzero(mism)[0]:
         gi = gids[r_i:r_i + 1]
         w = oracle.gate_weights(L[r_i:r_i + 1], gi)
-        o, _, _ = oracle.moe_forward_tokens(v, toks[r_i:r_i + 1], ids=gi, weights=w)
+        o, _, _ = oracle.moe_forward_tokens(v, toks[r_i:r_i + 1], ids=gi, weights=w, act_quant=act_quant)
         ref[r_i] = o[0]
     return ref
 
 
-def full_parity(inp, tol=None, layout="packed", **kw):
+def requant_alternatives(v, t, ids_row, w_row, margin):
+    """The H requantisation decisions of token t that sit within `margin` of a boundary, each
+    as the change of the token's output if it went the other way.
+
+    The library computes h = silu(g) * u in float32 (the fp8 matrix cores sum the block
+    products in float32) and the oracle in float64, so where h lies within the library's
+    rounding of an E4M3 rounding midpoint (a distance of `margin` steps of the value's binade)
+    both neighbouring codes are correct results, and likewise both scales where a block's
+    largest |h| lies within `margin` (relative) of a power-of-two scale boundary.  Returns a
+    list of output-space vectors: the weight of the row times W_down applied to the code (or
+    block) change."""
+    xq = oracle.fp8_quantize_rows(v.x[t:t + 1])[0]
+    rows = [(int(e), float(wj)) for e, wj in zip(ids_row, w_row)] + ([(v.E, 1.0)] if v.has_shared else [])
+    alts = []
+    for e, wt in rows:
+        wg, wu, wd = v.expert(e)
+        h = (oracle.silu(xq @ wg.T) * (xq @ wu.T))[0]
+        hq, kexp = oracle.fp8_quantize_rows(h[None, :])
+        hq, kexp = hq[0], kexp[0]
+        sc = np.repeat(np.ldexp(1.0, kexp), 128)
+        y = np.abs(h) / sc
+        _, ex = np.frexp(y)
+        step = np.ldexp(1.0, np.maximum(ex - 1, -6) - 3)
+        frac = y / step - np.floor(y / step)
+        for i in np.nonzero(np.abs(frac - 0.5) < margin)[0]:
+            down = np.floor(y[i] / step[i]) * step[i]
+            other = down + step[i] if abs(hq[i]) == down * sc[i] else down
+            alts.append(wt * (np.copysign(other * sc[i], h[i]) - hq[i]) * wd[:, i])
+        amax = np.abs(h).reshape(-1, 128).max(axis=1)
+        for b in range(len(amax)):
+            if amax[b] <= 0:
+                continue
+            for k2 in (kexp[b] + 1, kexp[b] - 1):
+                edge = np.ldexp(448.0, max(kexp[b], k2) - 1)
+                if abs(amax[b] / edge - 1.0) < margin and np.all(np.abs(h[128 * b:128 * b + 128]) <= np.ldexp(448.0, k2)):
+                    blk = h[128 * b:128 * b + 128] / np.ldexp(1.0, k2)
+                    alt = oracle.e4m3_round(blk) * np.ldexp(1.0, k2)
+                    alts.append(wt * wd[:, 128 * b:128 * b + 128] @ (alt - hq[128 * b:128 * b + 128]))
+    return alts
+
+
+def compare_outputs_requant(got, ref, v, ids, weights, tol, what="", margin=1e-3):
+    """compare_outputs for the fp8-activation mode: the whole output within tol, and every
+    token within tol of the oracle's output or of one of its equally correct alternatives:
+    the oracle's output with some of the token's near-boundary H requantisation decisions
+    (requant_alternatives) taken the other way, chosen greedily (each step takes the decision
+    whose change brings the oracle closest to the library).  Returns (rel Frobenius, worst
+    token error against the oracle's own decisions, tokens that needed an alternative)."""
+    err = oracle.rel_frobenius(got, ref)
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    per = num / den
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    assert err <= tol, f"{what}: rel Frobenius {err:.3e} > {tol}"
+    above = np.nonzero(per > tol)[0]
+    for t in above:
+        alts = requant_alternatives(v, t, ids[t], weights[t], margin)
+        assert alts, f"{what}: token {t} at {per[t]:.3e} with no requantisation decision near a boundary"
+        cur, left = ref[t].copy(), list(range(len(alts)))
+        best = per[t]
+        while left:
+            trial = [(float(np.linalg.norm(got[t] - cur - alts[q]) / max(np.linalg.norm(cur + alts[q]), 1e-30)), q)
+                     for q in left]
+            e_q, q = min(trial)
+            if e_q >= best:
+                break
+            best, cur = e_q, cur + alts[q]
+            left.remove(q)
+        assert best <= tol, f"{what}: token {t} at {per[t]:.3e}, best alternative {best:.3e} > {tol}"
+    return err, float(per.max()), len(above)
+
+
+def full_parity(inp, tol=None, layout="packed", act_quant=False, **kw):
+    """act_quant: run the library's fp8-activation mode; the oracle then quantises as the
+    library does when the m-tiles are above 16 rows (the mode's scope), else not."""
     c = inp.cfg
     tol = tol if tol is not None else TOL[c["w"]]
-    out, r, ctx = run_forward(inp, layout=layout, **kw)
+    out, r, ctx = run_forward(inp, layout=layout, act_quant=act_quant, **kw)
+    rows = kw.get("m_tile_rows") or moe.plan_describe(ctx["p"])["m_tile_rows"]
+    fp8_act = bool(act_quant) and rows > 16
     v = oracle.InputsView(inp)
     L, ids, gids, mism = check_routing(v, r, c["k"], c["E"])
     check_permutation(r, c["k"], c["E"])
-    ref = oracle_reference(v, L, ids, gids, mism)
+    ref = oracle_reference(v, L, ids, gids, mism, act_quant=fp8_act)
     got = out_to_f64(out)
-    err, worst = compare_outputs(got, ref, tol, c.get("name", ""))
-    return dict(err=err, worst=worst, near_tie_flips=int(mism.sum()), out=out, r=r, ctx=ctx)
+    if fp8_act:
+        ids_used = np.where(mism[:, None], gids, ids)
+        w_used = oracle.gate_weights(L, ids_used)
+        err, worst, n_above = compare_outputs_requant(got, ref, v, ids_used, w_used, tol, c.get("name", ""))
+    else:
+        err, worst = compare_outputs(got, ref, tol, c.get("name", ""))
+    return dict(err=err, worst=worst, near_tie_flips=int(mism.sum()), out=out, r=r, ctx=ctx, v=v, fp8_act=fp8_act,
+                routing=(L, ids, gids, mism))

@@ -27,7 +27,7 @@ def test_exports_every_header_function(L):
 
 
 def test_version_and_strings(L):
-    assert moe.abi_version() == 3
+    assert moe.abi_version() == 4
     for code, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARGUMENT"), (2, "MOE_ERR_UNSUPPORTED"),
                        (3, "MOE_ERR_WORKSPACE_TOO_SMALL"), (4, "MOE_ERR_HIP"), (5, "MOE_ERR_DEVICE_FAULT")]:
         assert moe.status_string(code) == name
@@ -90,6 +90,29 @@ def test_plan_describe_reports_the_m_tile(L, kw, rows):
     assert info["router_k_split"] in (1, 2, 4, 8)
     T, k, E = kw["T"], kw["k"], kw["E"]
     assert info["max_m_tiles"] >= min(T * k, E)
+
+
+def test_fp8_activation_mode_rules(L):
+    """act_quant: 0 or 1 (else INVALID), 1 only with fp8 weights (else UNSUPPORTED); the plan
+    reports fp8 activations exactly when the m-tiles are above 16 rows."""
+    for bad in (2, -1):
+        p = moe.problem(512, 7168, 2048, 256, 8, 1, w="fp8")
+        p.act_quant = bad
+        assert ws_size(p)[0] == INVALID
+    assert ws_size(moe.problem(512, 2048, 512, 256, 8, act_quant=True))[0] == UNSUPPORTED
+    assert ws_size(moe.problem(64, 256, 256, 8, 2, act="f32", w="f32", act_quant=True))[0] == UNSUPPORTED
+    for T, want in ((1, 0), (64, 0), (512, 1), (4096, 1)):
+        plan = moe.plan_describe(moe.problem(T, 7168, 2048, 256, 8, 1, w="fp8", act_quant=True))
+        assert plan["fp8_activations"] == want, T
+        assert (plan["m_tile_rows"] > 16) == bool(want)
+        assert moe.plan_describe(moe.problem(T, 7168, 2048, 256, 8, 1, w="fp8"))["fp8_activations"] == 0
+    # the fp8-activation workspace holds the E4M3 hidden rows and block scales; H shrinks to one
+    # byte per value
+    rc0, plain = ws_size(moe.problem(4096, 7168, 2048, 256, 8, 1, w="fp8"))
+    rc1, quant = ws_size(moe.problem(4096, 7168, 2048, 256, 8, 1, w="fp8", act_quant=True))
+    assert rc0 == rc1 == 0
+    rows_h = 4096 * 9
+    assert quant == pytest.approx(plain - rows_h * 2048 + 4096 * 7168 + 4096 * 56 + rows_h * 16, abs=4096)
 
 
 def test_tile_overrides_are_validated(L):

@@ -1,7 +1,8 @@
 """Benchmark of the MoE-layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--T T]
-                    [--configs LIST | --configs none] [--no-cpu-baseline]
+                    [--configs LIST | --configs none] [--no-cpu-baseline] [--fp8act]
+    python bench.py --item-trace [--config NAME] [--T T] [--fp8act]
 
 A step is one moe_forward call (the whole layer: route, permute, grouped SwiGLU
 GEMM, combine) over one batch of seeded synthetic input already resident in HBM.
@@ -57,6 +58,10 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--schedule", type=int, default=0)
+    ap.add_argument("--item-trace", action="store_true",
+                    help="instead: print the per-item trace summary of one forward of the headline workload")
+    ap.add_argument("--fp8act", action="store_true",
+                    help="headline workload in the fp8-activation mode (fp8-weight workloads only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead: time a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -278,6 +283,68 @@ def measure(wl, name, T, steps, warmup, copies=0, grid=0, schedule=0, want_input
     return res
 
 
+ITEM_KINDS = {0: "clear", 1: "router", 2: "topk", 3: "shared_gateup", 4: "scatter", 5: "gateup", 6: "down",
+              7: "combine", 8: "act_quant"}
+
+
+def item_trace(wl, name, T, act_quant=False):
+    """Per-item trace of one forward (moe_launch_options.trace): the span of the launch, the
+    busy share of the workgroups (item time over workgroups x span; the rest is waiting for a
+    dependency or for the queue), the gaps between consecutive items of a workgroup, and per
+    item kind the count, durations, tile-loop time and the first start / last end (us from
+    the launch's first item)."""
+    import numpy as np
+    import torch
+
+    import routed_grouped_gemm_amd as moe
+    from devinputs import tensor
+
+    key, cfg, inp = wl.inputs(name, T)
+    W = wl.device_weights(key, inp)
+    p = moe.problem(cfg["T"], cfg["d"], cfg["n"], cfg["E"], cfg["k"], cfg["shared"], cfg["act"], cfg["w"],
+                    layout="packed", act_quant=act_quant)
+    x, wr, bias = tensor(inp.hidden), tensor(inp.w_router), tensor(inp.bias)
+    ws = moe.alloc_workspace(p)
+    tr = torch.zeros(4 * 400000, dtype=torch.int64, device="cuda")
+    for _ in range(5):
+        moe.forward(p, x, wr, bias, W, ws)
+    torch.cuda.synchronize()
+    moe.forward(p, x, wr, bias, W, ws, trace=tr)
+    torch.cuda.synchronize()
+    assert moe.last_device_error(ws) == 0
+    rec = tr.view(-1, 4).cpu().numpy().astype(np.uint64)
+    rec = rec[rec[:, 1] > 0]
+    t0 = rec[:, 0].min()
+    start = (rec[:, 0] - t0).astype(np.float64) / 100.0  # the device clock runs at 100 MHz
+    end = (rec[:, 1] - t0).astype(np.float64) / 100.0
+    kind = (rec[:, 3] & 0xffffffff).astype(int)
+    wg = (rec[:, 3] >> 32).astype(int)
+    l0 = ((rec[:, 2] >> 32) & 0xffff).astype(np.float64) / 100.0
+    l1 = ((rec[:, 2] >> 48) & 0xffff).astype(np.float64) / 100.0
+    span = float(end.max())
+    ngrid = int(wg.max()) + 1
+    gaps = []
+    for w in range(ngrid):
+        m = np.nonzero(wg == w)[0]
+        o = m[np.argsort(start[m])]
+        gaps += list(start[o][1:] - end[o][:-1])
+    out = dict(workload=name, T=cfg["T"], fp8_activations=bool(moe.plan_describe(p)["fp8_activations"]),
+               span_us=round(span, 1), workgroups=ngrid, items=int(len(rec)),
+               busy_share=round(float((end - start).sum() / (ngrid * span)), 3),
+               gap_between_items_us={"mean": round(float(np.mean(gaps)), 2) if gaps else 0.0,
+                                     "p90": round(float(np.percentile(gaps, 90)), 2) if gaps else 0.0},
+               kinds={})
+    for k in sorted(set(kind.tolist())):
+        m = kind == k
+        d = end[m] - start[m]
+        loop = np.where(l1[m] > 0, l1[m] - l0[m], 0.0)
+        out["kinds"][ITEM_KINDS.get(k, str(k))] = dict(
+            n=int(m.sum()), dur_mean_us=round(float(d.mean()), 2), dur_max_us=round(float(d.max()), 2),
+            tile_loop_mean_us=round(float(loop.mean()), 2), first_start_us=round(float(start[m].min()), 1),
+            last_end_us=round(float(end[m].max()), 1))
+    return out
+
+
 def parse_entry(e):
     """NAME[@T][:static][:fp8act] -> (name, T, static, fp8act)"""
     head, *flags = e.split(":")
@@ -302,8 +369,11 @@ def main():
     if not os.path.exists(moe.LIB_PATH):
         raise SystemExit(f"{moe.LIB_PATH} is not built: run `python -m routed_grouped_gemm_amd.build` first")
     wl = Workloads()
+    if a.item_trace:
+        print(json.dumps(item_trace(wl, a.config, a.T, a.fp8act)), flush=True)
+        return
     head, cfg, inp = measure(wl, a.config, a.T, a.steps, a.warmup, copies=a.copies, grid=a.grid,
-                             schedule=a.schedule, want_inputs=True)
+                             schedule=a.schedule, want_inputs=True, act_quant=a.fp8act)
     roof = {"bound": head["roofline_bound"]}
     if head["roofline_bound"] == "hbm":
         roof.update(achieved=head["GB_s"], peak=HBM_PEAK_GBS, unit="GB/s", frac=head["hbm_frac"])
@@ -324,6 +394,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32" if cfg["act"] == "f32" else "bf16",
         "data": "synthetic",
         "config": {"workload": cfg["name"], "T": cfg["T"], "d": cfg["d"], "E": cfg["E"], "k": cfg["k"],
+                   "fp8_activations": head["fp8_activations"],
                    "n": cfg["n"], "shared_experts": cfg["shared"], "act": cfg["act"], "weights": cfg["w"],
                    "weight_layout": "packed (moe_pack_weights at load time)",
                    "experts_touched": head["experts_touched"], "m_tile_rows": head["m_tile_rows"],

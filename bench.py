@@ -123,6 +123,11 @@ def profile_name(workload, T):
     return f"moe_persistent_{workload}" + ("" if T is None else f"_T{T}")
 
 
+def synth_default_T(name):
+    import synth
+    return synth.config(name)["T"]
+
+
 def measured_traffic(workload, T=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary of this workload
     (DRAM read and write requests of the L2s, in 32-byte units), or None when there is none
@@ -266,7 +271,13 @@ def measure(wl, name, T, steps, warmup, copies=0, grid=0, schedule=0, want_input
     tfl = F / (avg_us * 1e-6) / 1e12
     t_hbm, t_mfma = B / (HBM_PEAK_GBS * 1e9), F / (peak_mfma * 1e12)
     wl_name = name + ("_fp8act" if plan["fp8_activations"] else "")
-    traffic = measured_traffic(wl_name, None if T is None or name != "large_fp8" else T)
+    # profiles exist per T for the large fp8 layer, else for the workload's own T only
+    if name == "large_fp8":
+        traffic = measured_traffic(wl_name, cfg["T"])
+    elif T is None or T == synth_default_T(name):
+        traffic = measured_traffic(wl_name)
+    else:
+        traffic = None
     res = dict(workload=name, T=cfg["T"], schedule="static" if schedule == 1 else "dynamic",
                fp8_activations=bool(plan["fp8_activations"]),
                m_tile_rows=plan["m_tile_rows"], experts_touched=touched,

@@ -2296,7 +2296,7 @@ typedef void (*KernelFn)(KParams);
 
 template <int WT> KernelFn pick_kernel(int mg) {
   if constexpr (WT == WQ8) {  // (m-tiles above 16 rows only, at most 128 rows)
-    return mg == 2 ? moe_persistent<WQ8, 2> : mg == 4 ? moe_persistent<WQ8, 4> : moe_persistent<WQ8, 8>;
+    return mg == 2 ? moe_persistent<WQ8, 2> : mg == 4 ? moe_persistent<WQ8, 4> : mg == 10 ? moe_persistent<WQ8, 10> : moe_persistent<WQ8, 8>;
   } else {
     switch (mg) {
       case 1: return moe_persistent<WT, 1>;

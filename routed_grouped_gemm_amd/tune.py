@@ -2,7 +2,8 @@
 
     python -m routed_grouped_gemm_amd.tune [--out PATH] [--report PATH] [--quick]
 
-For each weight dtype it times the layer, on random inputs of a real layer shape, at a
+For each weight dtype (and for fp8 weights also in the fp8-activation mode, which has its own
+m-tile kernels up to 160 rows) it times the layer, on random inputs of a real layer shape, at a
 sweep of token counts M, under every candidate tile (m-tile rows x group size of the
 grouped item order), and keeps per M the fastest candidate.  Neighbouring M with the same
 winner merge into one bucket; the bucket boundary between two winners is the geometric
@@ -33,14 +34,18 @@ import routed_grouped_gemm_amd as moe
 _PKG = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_OUT = os.path.join(_PKG, "csrc", "moe_tuned.h")
 
-# weight dtype -> (layer shape, token counts swept, candidate m-tile rows)
+# table row -> (layer shape, token counts swept, candidate m-tile rows); "fp8a": fp8 weights
+# with fp8 activations (moe_problem.act_quant)
 SWEEPS = {
     "bf16": (dict(d=2048, n=512, E=256, k=8), [16, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384],
              [16, 32, 64, 128, 160]),
-    "fp8": (dict(d=7168, n=2048, E=64, k=8), [2, 8, 32, 64, 128, 256, 512, 1024, 2048], [16, 32, 64, 128]),
+    "fp8": (dict(d=7168, n=2048, E=256, k=8), [1, 8, 32, 64, 128, 256, 512, 1024, 2048, 4096], [16, 32, 64, 128]),
+    "fp8a": (dict(d=7168, n=2048, E=256, k=8), [1, 8, 32, 64, 128, 256, 512, 1024, 2048, 4096],
+             [16, 32, 64, 128, 160]),
 }
 GROUPS = [1, 4]
-DTYPE_INDEX = {"f32": 0, "bf16": 1, "fp8": 2}
+ROWS = ("f32", "bf16", "fp8", "fp8a")   # rule lists of moe_tuned.h, in order
+WDTYPE = {"bf16": "bf16", "fp8": "fp8", "fp8a": "fp8"}
 
 
 def _weights(d, n, E, w, dev):
@@ -73,8 +78,9 @@ def _time(fn, steps, warmup):
     return statistics.median(s.elapsed_time(e) * 1e3 for s, e in ev)
 
 
-def sweep(w, quick=False, log=print):
-    shape, Ts, rows_list = SWEEPS[w]
+def sweep(row, quick=False, log=print):
+    shape, Ts, rows_list = SWEEPS[row]
+    w, aq = WDTYPE[row], row == "fp8a"
     d, n, E, k = shape["d"], shape["n"], shape["E"], shape["k"]
     dev = "cuda"
     torch.manual_seed(1234)
@@ -86,8 +92,12 @@ def sweep(w, quick=False, log=print):
     results = []
     floor, prev = 0, None  # a larger M never takes a smaller m-tile than a smaller M took
     for T in (Ts[::3] if quick else Ts):
-        p = moe.problem(T, d, n, E, k, 0, "bf16", w, layout="packed")
-        ws = moe.alloc_workspace(p, extra=8 << 20)
+        p = moe.problem(T, d, n, E, k, 0, "bf16", w, layout="packed", act_quant=aq)
+        # one workspace for every candidate tile: the w8a16 layout (bf16 H, the larger one) plus,
+        # for the fp8-activation tiles, their quantised hidden rows and block scales, plus room
+        # for the m-tile descriptors of the smallest tile
+        pw = moe.problem(T, d, n, E, k, 0, "bf16", w, layout="packed")
+        ws = moe.alloc_workspace(pw, extra=(8 << 20) + (T * d * 2 + T * k * n // 32 if aq else 0))
         x = xall[:T].contiguous()
         out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
         cand = {}
@@ -110,7 +120,7 @@ def sweep(w, quick=False, log=print):
         floor, prev = best[0], best
         mean = T * k / E
         results.append(dict(T=T, mean_rows=mean, best=best, us=cand, default=dkey))
-        log(f"[tune] {w} T={T} mean={mean:g}: best {best} {cand[best]:.1f} us (table {dkey} "
+        log(f"[tune] {row} T={T} mean={mean:g}: best {best} {cand[best]:.1f} us (table {dkey} "
             f"{cand.get(dkey, float('nan')):.1f} us)")
         del ws
     del W
@@ -141,10 +151,10 @@ def write_header(path, table, sources):
     lines = [
         "// moe_tuned.h -- the M-bucket tile table of the MoE-layer forward (included by moe_plan.h).",
         "//",
-        "// One rule list per weight dtype (f32, bf16, fp8): the first rule whose max_mean_rows is at",
-        "// least the problem's mean rows per routed expert (T*k/E) gives the m-tile size and the group",
-        "// size of the late phase's grouped item order.  Written by the tuner",
-        "// (python -m routed_grouped_gemm_amd.tune) from timings on the device:",
+        "// One rule list per weight dtype (f32, bf16, fp8, and fp8 weights with fp8 activations): the",
+        "// first rule whose max_mean_rows is at least the problem's mean rows per routed expert (T*k/E)",
+        "// gives the m-tile size and the group size of the late phase's grouped item order.  Written by",
+        "// the tuner (python -m routed_grouped_gemm_amd.tune) from timings on the device:",
     ] + [f"//   {s}" for s in sources] + [
         "#pragma once",
         "",
@@ -153,15 +163,15 @@ def write_header(path, table, sources):
         "",
         "struct TileRule {",
         "  float max_mean_rows;  // upper bound (inclusive) of the bucket's mean rows per routed expert",
-        "  int m_tile_rows;      // 16, 32, 64, 128 or 160 (fp8: at most 128)",
+        "  int m_tile_rows;      // 16, 32, 64, 128 or 160 (fp8 weights, bf16 activations: at most 128)",
         "  int group_m;          // late phase: m-tiles per group (m-tiles above 16 rows)",
         "};",
         "",
     ]
     n = max(len(v) for v in table.values())
     lines.append(f"constexpr int kNumTileRules = {n};")
-    lines.append("constexpr TileRule kTileRules[3][kNumTileRules] = {")
-    for name in ("f32", "bf16", "fp8"):
+    lines.append(f"constexpr TileRule kTileRules[{len(ROWS)}][kNumTileRules] = {{")
+    for name in ROWS:
         rules = list(table[name])
         while len(rules) < n:
             rules.append(rules[-1])
@@ -184,13 +194,14 @@ def main():
     assert torch.cuda.is_available(), "the tuner runs on the GPU"
     report = [f"# Tile-table tuning ({datetime.date.today()}, {torch.cuda.get_device_name(0)})", ""]
     table, sources = {}, []
-    for w in ("bf16", "fp8"):
+    for w in ("bf16", "fp8", "fp8a"):
         res = sweep(w, quick=a.quick)
         shape = SWEEPS[w][0]
-        table[w] = rules_from(res, 128 if w == "fp8" else 160)
+        table[w] = rules_from(res, max(SWEEPS[w][2]))
+        label = "fp8 weights, fp8 activations" if w == "fp8a" else f"{w} weights"
         sources.append(f"{w}: d={shape['d']} n={shape['n']} E={shape['E']} k={shape['k']}, "
                        f"M in {[r['T'] for r in res]}")
-        report += [f"## {w} weights, d={shape['d']} n={shape['n']} E={shape['E']} k={shape['k']}", "",
+        report += [f"## {label}, d={shape['d']} n={shape['n']} E={shape['E']} k={shape['k']}", "",
                    "| T | mean rows | chosen (rows, group) | " + " | ".join(f"{c}" for c in res[0]["us"]) + " |",
                    "|---|---|---|" + "---|" * len(res[0]["us"])]
         for r in res:

@@ -101,11 +101,12 @@ def test_fp8_activation_mode_rules(L):
         assert ws_size(p)[0] == INVALID
     assert ws_size(moe.problem(512, 2048, 512, 256, 8, act_quant=True))[0] == UNSUPPORTED
     assert ws_size(moe.problem(64, 256, 256, 8, 2, act="f32", w="f32", act_quant=True))[0] == UNSUPPORTED
-    for T, want in ((1, 0), (64, 0), (512, 1), (4096, 1)):
+    for T in (1, 8, 64, 512, 4096):
         plan = moe.plan_describe(moe.problem(T, 7168, 2048, 256, 8, 1, w="fp8", act_quant=True))
-        assert plan["fp8_activations"] == want, T
-        assert (plan["m_tile_rows"] > 16) == bool(want)
+        assert plan["fp8_activations"] == int(plan["m_tile_rows"] > 16), T
         assert moe.plan_describe(moe.problem(T, 7168, 2048, 256, 8, 1, w="fp8"))["fp8_activations"] == 0
+    assert moe.plan_describe(moe.problem(1, 7168, 2048, 256, 8, 1, w="fp8", act_quant=True))["fp8_activations"] == 0
+    assert moe.plan_describe(moe.problem(4096, 7168, 2048, 256, 8, 1, w="fp8", act_quant=True))["fp8_activations"] == 1
     # the fp8-activation workspace holds the E4M3 hidden rows and block scales; H shrinks to one
     # byte per value
     rc0, plain = ws_size(moe.problem(4096, 7168, 2048, 256, 8, 1, w="fp8"))
@@ -126,7 +127,7 @@ def test_tile_overrides_are_validated(L):
                                 VP(1 << 24), 1 << 30, None, ctypes.byref(o)) == want
     pf = moe.problem(16, 2048, 512, 256, 8, w="fp8", layout="packed")
     Wf = moe.Weights(*([1 << 21] * 6 + [None] * 6))
-    o = moe.LaunchOptions(0, 0, None, 0, 160, 0)   # no 160-row fp8 kernel
+    o = moe.LaunchOptions(0, 0, None, 0, 160, 0)   # no 160-row fp8 kernel with bf16 activations
     assert L.moe_forward_ex(ctypes.byref(pf), VP(1 << 20), VP(1 << 20), None, ctypes.byref(Wf), VP(3 << 20), None,
                             VP(1 << 24), 1 << 30, None, ctypes.byref(o)) == INVALID
 
@@ -134,14 +135,15 @@ def test_tile_overrides_are_validated(L):
 def test_tile_table_is_well_formed(L):
     """The compiled-in tile table: mean-row bounds increase, tiles are valid for the dtype, and the
     chosen tile grows with the mean rows per expert."""
-    for w in ("f32", "bf16", "fp8"):
+    for w, aq in (("f32", False), ("bf16", False), ("fp8", False), ("fp8", True)):
         act = "f32" if w == "f32" else "bf16"
         prev = 0
         for T in (1, 16, 64, 256, 1024, 4096, 16384, 65536):
-            info = moe.plan_describe(moe.problem(T, 2048, 512, 256, 8, act=act, w=w))
-            assert info["m_tile_rows"] in ((16, 32, 64, 128) if w == "fp8" else (16, 32, 64, 128, 160))
+            info = moe.plan_describe(moe.problem(T, 2048, 512, 256, 8, act=act, w=w, act_quant=aq))
+            assert info["m_tile_rows"] in ((16, 32, 64, 128) if w == "fp8" and not aq else (16, 32, 64, 128, 160))
             assert 1 <= info["group_m"] <= 64
             assert info["m_tile_rows"] >= prev
+            assert info["fp8_activations"] == int(aq and info["m_tile_rows"] > 16)
             prev = info["m_tile_rows"]
 
 

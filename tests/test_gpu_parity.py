@@ -97,6 +97,7 @@ AQ_CASES = [
     (34, 300, 768, 512, 16, 4, 1, False, 128),
     (35, 77, 256, 256, 3, 1, 1, False, 128),    # ragged, one routed slot
     (36, 500, 1024, 256, 8, 2, 1, True, 128),   # several 128-row m-tiles per expert
+    (39, 500, 1024, 256, 8, 2, 1, True, 160),   # 160-row m-tiles, ~125 rows per expert
 ]
 
 

@@ -78,6 +78,19 @@ def _time(fn, steps, warmup):
     return statistics.median(s.elapsed_time(e) * 1e3 for s, e in ev)
 
 
+def choose(cand, floor, prev, dkey, margin=0.02):
+    """The winner at one M: the fastest candidate (rows, group) whose m-tile is at least `floor`
+    (the previous M's winner), except that the previous M's winner, or else the current table's
+    choice `dkey`, is kept unless the fastest is more than `margin` faster (so timing noise
+    does not split buckets)."""
+    allowed = {c: t for c, t in cand.items() if c[0] >= floor}
+    best = min(allowed, key=allowed.get)
+    for keep in (prev, dkey):
+        if keep in allowed and allowed[best] > (1.0 - margin) * allowed[keep]:
+            return keep
+    return best
+
+
 def sweep(row, quick=False, log=print):
     shape, Ts, rows_list = SWEEPS[row]
     w, aq = WDTYPE[row], row == "fp8a"
@@ -109,14 +122,7 @@ def sweep(row, quick=False, log=print):
                 cand[(rows, gm)] = us
         default = moe.plan_describe(p)
         dkey = (default["m_tile_rows"], default["group_m"])
-        allowed = {c: t for c, t in cand.items() if c[0] >= floor}
-        best = min(allowed, key=allowed.get)
-        # a candidate replaces the previous M's winner, or else the current table's choice, only
-        # when more than 2% faster
-        for keep in (prev, dkey):
-            if keep in allowed and allowed[best] > 0.98 * allowed[keep]:
-                best = keep
-                break
+        best = choose(cand, floor, prev, dkey)
         floor, prev = best[0], best
         mean = T * k / E
         results.append(dict(T=T, mean_rows=mean, best=best, us=cand, default=dkey))

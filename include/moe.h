@@ -180,8 +180,8 @@ typedef struct {
   int32_t schedule;
   void *trace;
   int64_t trace_bytes;
-  int32_t m_tile_rows;  /* 0 = the tuned M-bucket table's; else 16, 32, 64, 128 or 160 (not 160
-                           with fp8 weights).  The workspace must be sized for the chosen tile:
+  int32_t m_tile_rows;  /* 0 = the tuned M-bucket table's; else 16, 32, 64, 128 or 160.
+                           The workspace must be sized for the chosen tile:
                            moe_workspace_size reports the table's (a smaller tile needs a few
                            KB more for its m-tile descriptors), else MOE_ERR_WORKSPACE_TOO_SMALL */
   int32_t group_m;      /* 0 = the table's; else 1..64 m-tiles per group of the grouped order */

@@ -74,12 +74,16 @@ template <> struct Ty<WQ8> { static constexpr int KU = 64, WSZ = 1, ASZ = 1; };
 
 // per-kernel tile shape: MG 16-token groups per m-tile, NF weight fragments per wave,
 // FL 16-byte weight loads per fragment per K chunk
+#ifndef MOE_FP8_FOLD_MG
+#define MOE_FP8_FOLD_MG 4
+#endif
 template <int WT, int MG> struct Shape {
   static constexpr int NF = MG == 1 ? 2 : 4;
-  // register/LDS buffers: three (two K chunks in flight) where the registers allow it,
-  // else two (one chunk in flight, longer chunks)
+  // register/LDS buffers: three (two K chunks in flight) where registers and LDS allow it,
+  // else two (one chunk in flight): the 32-row fp8 tiles (registers) and the 160-row fp8
+  // tiles (three 40 KB activation stages and the routing scratch exceed the 160 KB of LDS)
 #ifndef MOE_NBUF
-#define MOE_NBUF(WT, MG) ((MG == 2 && WT == WFP8) ? 2 : 3)
+#define MOE_NBUF(WT, MG) ((WT == WFP8 && (MG == 2 || MG == 10)) ? 2 : 3)
 #define MOE_FL(WT, MG) ((WT != WFP8 && MG == 1) ? 4 : 2)
 #endif
   static constexpr int NBUF = MOE_NBUF(WT, MG);
@@ -333,6 +337,19 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// 8 OCP e4m3 codes times a block scale -> 8 bf16: each decoded value (exact in fp32) is
+// multiplied by the scale in fp32 and the product rounded to bf16, nearest even (the hardware's
+// scaled conversions take only the scale's exponent, so the multiply is explicit)
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16_scaled(uint32_t a, uint32_t b, float s) {
+  const f2v p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)a, false);
+  const f2v p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)a, true);
+  const f2v p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);
+  const f2v p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, true);
+  return bf16x8{static_cast<__bf16>(p0.x * s), static_cast<__bf16>(p0.y * s), static_cast<__bf16>(p1.x * s),
+                static_cast<__bf16>(p1.y * s), static_cast<__bf16>(p2.x * s), static_cast<__bf16>(p2.y * s),
+                static_cast<__bf16>(p3.x * s), static_cast<__bf16>(p3.y * s)};
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
@@ -453,6 +470,55 @@ template <int WT, int MG> struct Core {
         if (FULL || b == 0 || b < ngroups) {
 #pragma unroll
           for (int a = 0; a < NF; ++a) acc[a][b] += mfma_fp8x8(W[a][0], W[a][1], cur.lo, cur.hi, cur.s) * sw[a];
+        }
+      }
+    } else if constexpr (WT == WFP8 && MG >= MOE_FP8_FOLD_MG) {
+      // fp8 weights, scale folded: the 16 rows of a fragment lie in one 128-row scale block, so
+      // each fragment has one block scale per 128-wide K block; its codes are decoded, multiplied
+      // by that scale and rounded to bf16 once per chunk, shared by the MG token groups, and the
+      // MFMAs accumulate straight into acc (no per-block partial sums to scale)
+      constexpr int BPC = FL / 2;  // 128-wide scale blocks per chunk (a step is 64 codes)
+      bf16x8 D[NF][FL][2];
+#pragma unroll
+      for (int blk = 0; blk < BPC; ++blk) {
+#pragma unroll
+        for (int a = 0; a < NF; ++a) {
+          const float s = ld_uniform(sc[a] + c * BPC + blk);
+#pragma unroll
+          for (int ff = 0; ff < 2; ++ff) {
+            const uint4 &w = W[a][blk * 2 + ff];
+            D[a][blk * 2 + ff][0] = fp8x8_to_bf16_scaled(w.x, w.y, s);
+            D[a][blk * 2 + ff][1] = fp8x8_to_bf16_scaled(w.z, w.w, s);
+          }
+        }
+      }
+      // the activation operands of the FL * MG (step, group) pairs, LA pairs ahead of their
+      // MFMAs; a step's 64 K positions of this lane are two 16-byte columns of the row
+      constexpr int NP = FL * MG, LA = NP < 3 ? NP : 3;
+      struct Aop {
+        uint4 a0, a1;
+      };
+      auto rd = [&](int t) {
+        const int f = t / MG, b = t % MG, r = b * 16 + j, c0 = f * 8 + 2 * g;
+        Aop o;
+        o.a0 = *reinterpret_cast<const uint4 *>(A + r * RB + ((c0 ^ (r & (NCOL - 1))) << 4));
+        o.a1 = *reinterpret_cast<const uint4 *>(A + r * RB + (((c0 + 1) ^ (r & (NCOL - 1))) << 4));
+        return o;
+      };
+      Aop av[LA];
+#pragma unroll
+      for (int t = 0; t < LA; ++t) av[t] = rd(t);
+#pragma unroll
+      for (int t = 0; t < NP; ++t) {
+        const int f = t / MG, b = t % MG;
+        const Aop cur = av[t % LA];
+        if (t + LA < NP) av[t % LA] = rd(t + LA);
+        if (FULL || b == 0 || b < ngroups) {
+#pragma unroll
+          for (int a = 0; a < NF; ++a) {
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(D[a][f][0], __builtin_bit_cast(bf16x8, cur.a0), acc[a][b], 0, 0, 0);
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(D[a][f][1], __builtin_bit_cast(bf16x8, cur.a1), acc[a][b], 0, 0, 0);
+          }
         }
       }
     } else if constexpr (WT == WFP8) {
@@ -648,6 +714,9 @@ template <int WT, int MG> struct Core {
 template <int WT, int MG> struct ActBuf {
   using RC = Core<(WT == WF32 ? WF32 : WBF16), router_groups(MG)>;
   static constexpr int BYTES = (MG > 1 && RC::BUF > Core<WT, MG>::BUF) ? RC::BUF : Core<WT, MG>::BUF;
+  // the third stage: the expert tiles' own where they have three stages, else only the router
+  // tiles' (whose pipeline always has three)
+  static constexpr int BYTES2 = Shape<WT, MG>::NBUF >= 3 ? BYTES : (MG > 1 && RC::BUF > 16 ? RC::BUF : 16);
 };
 
 template <int WT, int MG> struct Smem {
@@ -1968,10 +2037,13 @@ void moe_persistent(KParams P) {
   __shared__ Smem<WT, MG> sm;
   __shared__ __attribute__((aligned(16))) char act0[ActBuf<WT, MG>::BYTES];
   __shared__ __attribute__((aligned(16))) char act1[ActBuf<WT, MG>::BYTES];
-  __shared__ __attribute__((aligned(16))) char act2[ActBuf<WT, MG>::BYTES];
+  __shared__ __attribute__((aligned(16))) char act2[ActBuf<WT, MG>::BYTES2];
   __shared__ __attribute__((aligned(16))) char act3[Shape<WT, MG>::NBUF >= 4 ? ActBuf<WT, MG>::BYTES : 16];
   __shared__ __attribute__((aligned(16))) uint8_t scl[ScaleBuf<WT, MG>::BYTES];
   const Lds3 lb{act0, act1, act2, act3, scl};
+  static_assert(sizeof(Smem<WT, MG>) + 2 * ActBuf<WT, MG>::BYTES + ActBuf<WT, MG>::BYTES2 + sizeof(act3) +
+                        ScaleBuf<WT, MG>::BYTES + 64 <= 160 * 1024,
+                "LDS of one workgroup above the 160 KB of a CU");
   const int tid = threadIdx.x;
   int *ctrl = P.ctrl;
   int *err = ctrl + kSlotInts * C_ERR;
@@ -2295,7 +2367,7 @@ __global__ void pack_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ d
 typedef void (*KernelFn)(KParams);
 
 template <int WT> KernelFn pick_kernel(int mg) {
-  if constexpr (WT == WQ8) {  // (m-tiles above 16 rows only, at most 128 rows)
+  if constexpr (WT == WQ8) {  // (m-tiles above 16 rows only)
     return mg == 2 ? moe_persistent<WQ8, 2> : mg == 4 ? moe_persistent<WQ8, 4> : mg == 10 ? moe_persistent<WQ8, 10> : moe_persistent<WQ8, 8>;
   } else {
     switch (mg) {
@@ -2304,9 +2376,7 @@ template <int WT> KernelFn pick_kernel(int mg) {
       case 4: return moe_persistent<WT, 4>;
       default: break;
     }
-    if constexpr (WT != WFP8) {  // (no 160-row fp8 kernel: see choose_tiles)
-      if (mg == 10) return moe_persistent<WT, 10>;
-    }
+    if (mg == 10) return moe_persistent<WT, 10>;
     return moe_persistent<WT, 8>;
   }
 }

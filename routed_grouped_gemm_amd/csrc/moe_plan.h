@@ -162,9 +162,7 @@ inline Tiles tiles_for(const moe_problem *p, int mg, int group_m) {
 // The tile from the M-bucket table (moe_tuned.h), keyed by the mean rows per routed expert.
 // The row count of an expert spreads around the mean by about its square root, so a bucket's
 // m-tile is chosen for most experts to fit in one m-tile (each extra m-tile re-reads the
-// expert's weights); the fp8 w8a16 kernels stop at 128 rows (their registers), the
-// fp8-activation kernels at 160.  Rule lists: f32, bf16, fp8 weights, fp8 weights with fp8
-// activations.
+// expert's weights).  Rule lists: f32, bf16, fp8 weights, fp8 weights with fp8 activations.
 inline int tile_table_row(const moe_problem *p) {
   if (p->w_dtype == MOE_F32) return 0;
   if (p->w_dtype == MOE_BF16) return 1;
@@ -190,7 +188,6 @@ inline bool override_tiles(const moe_problem *p, int m_tile_rows, int group_m, T
   if (m_tile_rows != 0) {
     const int r = m_tile_rows;
     if (r != 16 && r != 32 && r != 64 && r != 128 && r != 160) return false;
-    if (r == 160 && p->w_dtype == MOE_FP8_E4M3 && p->act_quant != MOE_AQ_FP8) return false;
     *t = tiles_for(p, r / 16, t->group_m);
   }
   if (group_m != 0) t->group_m = group_m;

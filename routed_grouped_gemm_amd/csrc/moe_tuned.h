@@ -14,20 +14,20 @@ namespace {
 
 struct TileRule {
   float max_mean_rows;  // upper bound (inclusive) of the bucket's mean rows per routed expert
-  int m_tile_rows;      // 16, 32, 64, 128 or 160 (fp8 weights, bf16 activations: at most 128)
+  int m_tile_rows;      // 16, 32, 64, 128 or 160
   int group_m;          // late phase: m-tiles per group (m-tiles above 16 rows)
 };
 
-constexpr int kNumTileRules = 4;
+constexpr int kNumTileRules = 5;
 constexpr TileRule kTileRules[4][kNumTileRules] = {
     // f32
-    {{5.656854f, 16, 4}, {22.627417f, 64, 1}, {90.509668f, 128, 1}, {1e30f, 160, 4}},
+    {{5.656854f, 16, 4}, {45.254834f, 64, 1}, {90.509668f, 128, 1}, {1e30f, 160, 4}, {1e30f, 160, 4}},
     // bf16
-    {{5.656854f, 16, 4}, {22.627417f, 64, 1}, {90.509668f, 128, 1}, {1e30f, 160, 4}},
+    {{5.656854f, 16, 4}, {45.254834f, 64, 1}, {90.509668f, 128, 1}, {1e30f, 160, 4}, {1e30f, 160, 4}},
     // fp8
-    {{0.088388f, 16, 4}, {22.627417f, 32, 1}, {45.254834f, 64, 4}, {1e30f, 128, 4}},
+    {{0.088388f, 16, 4}, {22.627417f, 32, 1}, {45.254834f, 64, 4}, {90.509668f, 128, 4}, {1e30f, 160, 1}},
     // fp8a
-    {{0.088388f, 16, 4}, {45.254834f, 64, 1}, {90.509668f, 128, 4}, {1e30f, 160, 1}},
+    {{0.088388f, 16, 4}, {45.254834f, 64, 1}, {90.509668f, 128, 4}, {1e30f, 160, 1}, {1e30f, 160, 1}},
 };
 constexpr const char *kTileTableSource = "tuned on the device";
 

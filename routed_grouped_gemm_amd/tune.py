@@ -26,6 +26,7 @@ import datetime
 import math
 import os
 import statistics
+import sys
 
 import torch
 
@@ -39,7 +40,8 @@ DEFAULT_OUT = os.path.join(_PKG, "csrc", "moe_tuned.h")
 SWEEPS = {
     "bf16": (dict(d=2048, n=512, E=256, k=8), [16, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384],
              [16, 32, 64, 128, 160]),
-    "fp8": (dict(d=7168, n=2048, E=256, k=8), [1, 8, 32, 64, 128, 256, 512, 1024, 2048, 4096], [16, 32, 64, 128]),
+    "fp8": (dict(d=7168, n=2048, E=256, k=8), [1, 8, 32, 64, 128, 256, 512, 1024, 2048, 4096],
+            [16, 32, 64, 128, 160]),
     "fp8a": (dict(d=7168, n=2048, E=256, k=8), [1, 8, 32, 64, 128, 256, 512, 1024, 2048, 4096],
              [16, 32, 64, 128, 160]),
 }
@@ -169,7 +171,7 @@ def write_header(path, table, sources):
         "",
         "struct TileRule {",
         "  float max_mean_rows;  // upper bound (inclusive) of the bucket's mean rows per routed expert",
-        "  int m_tile_rows;      // 16, 32, 64, 128 or 160 (fp8 weights, bf16 activations: at most 128)",
+        "  int m_tile_rows;      // 16, 32, 64, 128 or 160",
         "  int group_m;          // late phase: m-tiles per group (m-tiles above 16 rows)",
         "};",
         "",
@@ -198,7 +200,8 @@ def main():
     ap.add_argument("--quick", action="store_true")
     a = ap.parse_args()
     assert torch.cuda.is_available(), "the tuner runs on the GPU"
-    report = [f"# Tile-table tuning ({datetime.date.today()}, {torch.cuda.get_device_name(0)})", ""]
+    report = [f"# Tile-table tuning ({datetime.date.today()}, {torch.cuda.get_device_name(0)})", "",
+              "Command: `python -m routed_grouped_gemm_amd.tune " + " ".join(sys.argv[1:]) + "`", ""]
     table, sources = {}, []
     for w in ("bf16", "fp8", "fp8a"):
         res = sweep(w, quick=a.quick)

@@ -76,7 +76,7 @@ def test_large_fp8_forward(large, oracle_all_rows, T):
                           sh_s_gate=inp_full.sh_s_gate, sh_s_up=inp_full.sh_s_up, sh_s_down=inp_full.sh_s_down)
     p = moe.problem(T, cfg["d"], cfg["n"], cfg["E"], cfg["k"], 1, "bf16", "fp8", layout="packed")
     rows = moe.plan_describe(p)["m_tile_rows"]
-    assert rows in (16, 32, 64, 128)  # (the tuned table's choice; fp8 tiles stop at 128 rows)
+    assert rows in (16, 32, 64, 128, 160)  # (the tuned table's choice)
     x = x_full[:T].contiguous()
     ws = moe.alloc_workspace(p)
     out, r = moe.forward(p, x, wr, b, W, ws, route_out=True)

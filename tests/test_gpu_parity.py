@@ -64,6 +64,7 @@ ADHOC = [
     (28, 300, 256, 512, 16, 4, "f32", "f32", 1, False, 128),   # fp32 128-row tiles, 75 rows/expert
     (29, 400, 512, 256, 16, 4, "bf16", "fp8", 1, True, 128),   # fp8 128-row tiles, 100 rows/expert
     (30, 250, 512, 512, 8, 4, "f32", "f32", 0, True, 160),     # fp32 160-row tiles, several per expert
+    (40, 700, 1024, 256, 8, 2, "bf16", "fp8", 1, True, 160),  # fp8 160-row tiles (two stages), ~175 rows/expert
 ]
 
 

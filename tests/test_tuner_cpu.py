@@ -63,6 +63,5 @@ def test_compiled_in_table_has_the_tuner_form():
         assert len(rules) == n
         bounds = [b for b, _, _ in rules]
         assert bounds == sorted(bounds) and bounds[-1] >= 1e29
-        limit = 128 if name == "fp8" else 160
-        assert all(r in (16, 32, 64, 128, 160) and r <= limit and 1 <= g <= 64 for _, r, g in rules)
+        assert all(r in (16, 32, 64, 128, 160) and 1 <= g <= 64 for _, r, g in rules)
         assert [r for _, r, _ in rules] == sorted(r for _, r, _ in rules)

@@ -948,21 +948,45 @@ __device__ __forceinline__ void logits_item_tile(const KParams &P, int i, SM &sm
     sc[a] = nullptr;
   }
   f4 acc[NF][RMG];
+  if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
   C::template run<false, 64>(acc, wrow, sc, reinterpret_cast<const char *>(P.x) + (size_t)kbeg * asz,
                              (size_t)P.d * asz, sm.rows, lb, kpart, (m + 15) >> 4);
+  if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
+  // The sums leave through LDS, so that a store covers whole runs of a token's row: per
+  // 16-token group, the wave's NF fragments (16 tokens x its EPW experts) go to its own slab
+  // of the routing scratch (unused by this item; rows padded by 4 floats against bank
+  // conflicts), and each lane then stores 4 consecutive experts of one token, LPR lanes
+  // covering the wave's contiguous 4 * EPW bytes of that token's row.  (A wave reads back
+  // only what its own lanes wrote, and its LDS operations complete in order.)
+  constexpr int EPW = 16 * NF, LPR = EPW / 4, RPI = 64 / LPR, SROW = EPW + 4;
+  static_assert(sizeof(sm.u) >= kWaves * 16 * SROW * sizeof(float), "router tile slab");
+  float *slab = reinterpret_cast<float *>(&sm.u) + wv * 16 * SROW;
+  float bv[4] = {0.f, 0.f, 0.f, 0.f};
+  const int col = (lane % LPR) * 4, e = e0 + col;
+  if (P.bias && S == 1) {
 #pragma unroll
-  for (int a = 0; a < NF; ++a) {
+    for (int z = 0; z < 4; ++z) bv[z] = e + z < P.E ? P.bias[e + z] : 0.f;
+  }
+  float *const dst = S == 1 ? P.logits : P.lpart + (size_t)ks * P.T * P.E;
+  const bool vec = e + 3 < P.E && (P.E & 1) == 0;  // 8-byte aligned pairs, all four in range
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = e0 + 16 * a + 4 * g + r;
-      if (e >= P.E) continue;
-      const float bv = (P.bias && S == 1) ? P.bias[e] : 0.f;
+  for (int b = 0; b < RMG; ++b) {
+    if (b * 16 >= m) break;
 #pragma unroll
-      for (int b = 0; b < RMG; ++b) {
-        if (b * 16 + j >= m) continue;
-        const size_t t = (size_t)(t0 + b * 16 + j);
-        if (S == 1) st_coh(P.logits + t * P.E + e, acc[a][b][r] + bv);
-        else st_coh(P.lpart + ((size_t)ks * P.T + t) * P.E + e, acc[a][b][r]);
+    for (int a = 0; a < NF; ++a) *reinterpret_cast<f4 *>(slab + j * SROW + 16 * a + 4 * g) = acc[a][b];
+#pragma unroll
+    for (int q = 0; q < 16 / RPI; ++q) {
+      const int row = q * RPI + lane / LPR;
+      const f4 v = *reinterpret_cast<const f4 *>(slab + row * SROW + col);
+      if (b * 16 + row >= m || e >= P.E) continue;
+      float *p = dst + (size_t)(t0 + b * 16 + row) * P.E + e;
+      if (vec) {
+        st_coh64(p, (uint64_t)__float_as_uint(v[0] + bv[0]) | ((uint64_t)__float_as_uint(v[1] + bv[1]) << 32));
+        st_coh64(p + 2, (uint64_t)__float_as_uint(v[2] + bv[2]) | ((uint64_t)__float_as_uint(v[3] + bv[3]) << 32));
+      } else {
+#pragma unroll
+        for (int z = 0; z < 4; ++z)
+          if (e + z < P.E) st_coh(p + z, v[z] + bv[z]);
       }
     }
   }
@@ -1404,6 +1428,15 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
   }
 }
 
+// topk_tokens with its part loads sized for the router's actual K split (each load in flight
+// holds a slot of the wave's limited count of outstanding memory operations)
+template <int TPW, int SMAX, class SM>
+__device__ __forceinline__ void topk_tokens_parts(const KParams &P, int t0, int ntok, SM &sm) {
+  if (P.rt_split <= 2 || SMAX <= 2) topk_tokens<TPW, (SMAX < 2 ? SMAX : 2)>(P, t0, ntok, sm);
+  else if (P.rt_split <= 4 || SMAX <= 4) topk_tokens<TPW, (SMAX < 4 ? SMAX : 4)>(P, t0, ntok, sm);
+  else topk_tokens<TPW, SMAX>(P, t0, ntok, sm);
+}
+
 // K item c: top-k of kt_tok tokens.  When all tokens form one scatter chunk (n_kc == 1),
 // the last K item to finish (or the only one) builds the plan and scatters every token;
 // otherwise an item adds its per-expert counts to its chunk's histogram (integer atomics:
@@ -1416,9 +1449,9 @@ __device__ __forceinline__ void topk_item(const KParams &P, int c, SM &sm) {
   if (P.phases & PH_IDS_GIVEN) {
     for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = checked_id(P.ids[(size_t)t0 * k + q], E);  // caller's input
   } else if (P.kt_tok == kTopkTokensSmall) {
-    topk_tokens<kTopkTokensSmall / kWaves, SMAX>(P, t0, ntok, sm);
+    topk_tokens_parts<kTopkTokensSmall / kWaves, SMAX>(P, t0, ntok, sm);
   } else {
-    topk_tokens<kTopkTokens / kWaves, SMAX>(P, t0, ntok, sm);
+    topk_tokens_parts<kTopkTokens / kWaves, SMAX>(P, t0, ntok, sm);
   }
   __syncthreads();
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();

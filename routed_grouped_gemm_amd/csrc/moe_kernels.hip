@@ -105,7 +105,7 @@ struct KParams {
   int late;       // 1: gate/up and down items from the per-XCD queues, grouped order (see the kernel)
   int group_m;    // late phase: m-tiles per group
   int aq;         // 1: fp8 activations (Q items quantise the hidden rows; H is requantised)
-  int n_Q;        // activation-quantisation items (bound to workgroups, after the router items)
+  int n_Q;        // activation-quantisation items (ticketed, after the scatter items)
   int xs_stride, hs_stride;  // bytes per row of the hidden / H block-scale arrays
   const void *x, *wr;
   const float *bias;
@@ -353,7 +353,10 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16_scaled(uint32_t a, uint32_t b, f
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u = g / (1 + e^-g) * u, the quotient by the hardware reciprocal (about 1 ulp of
+// float32, far below the rounding of H to the activation dtype; an IEEE division costs a
+// dozen vector instructions, 80 of them per lane at the end of a 160-row gate/up item)
+__device__ __forceinline__ float silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
 
 // monotone map float -> uint32 (after -0.0 -> +0.0): larger float -> larger key
 __device__ __forceinline__ uint32_t ordered_key(float v) {
@@ -593,10 +596,13 @@ template <int WT, int MG> struct Core {
   // packed expert weights, 64 for the row-major router rows)
   // sbase, sstride (fp8 activations only): the rows' block scales, one byte per 128-wide
   // block, sstride bytes (a multiple of 4) per row; staged in LDS (lb.sl) before the K loop
+  // sig: the completion counter of this workgroup's previous item, whose result stores may
+  // still be in flight (null: none); it is incremented once every wave's stores have
+  // completed, after this item's first loads are issued, so that their latency overlaps
   template <bool COH, int WSTEP>
   __device__ static void run(f4 (&acc)[NF][MG], const char *const (&wrow)[NF], const float *const (&sc)[NF],
                              const char *abase, size_t arow_bytes, const int *rows, const Lds3 &lb, int K,
-                             int ngroups, const uint8_t *sbase = nullptr, int sstride = 0) {
+                             int ngroups, const uint8_t *sbase = nullptr, int sstride = 0, int *sig = nullptr) {
     const int tid = otid(), lane = tid & 63, g = lane >> 4, j = lane & 15;
     const int wv = uni(tid >> 6);
     const int nch = K / KC;
@@ -658,13 +664,16 @@ template <int WT, int MG> struct Core {
         for (int s = 0; s < NDMA; ++s) dma16<COH>(arsrc, aoff[s], off, buf + (s * kWaves + wv) * 1024);
       }
     };
+    // (expert weights are read once: nontemporal; the router's rows are read by every router
+    // tile of the XCD, so they load with the default policy and stay in its L2)
+    constexpr int wpol = WSTEP == kWStep ? kCpolNt : 0;
     auto ldw = [&](uint4(&W)[NF][FL], int c) {
       const int off = min(c, nch - 1) * (FL * WSTEP);
 #pragma unroll
       for (int f = 0; f < FL; ++f)
 #pragma unroll
         for (int a = 0; a < NF; ++a)
-          W[a][f] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc[a], woff[a], off + f * WSTEP, kCpolNt));
+          W[a][f] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc[a], woff[a], off + f * WSTEP, wpol));
     };
     // small tiles compute every token group (rows past the tile's end repeat its last
     // row, valid data whose results are not stored); large tiles skip absent groups,
@@ -684,6 +693,13 @@ template <int WT, int MG> struct Core {
     for (int st = 0; st < NBUF - 1; ++st) {
       dma(st, stage_buf(lb, st));
       ldw(W[st], st);
+    }
+    if (sig != nullptr) {
+      // every operation older than the prologue's loads (the previous item's stores) has
+      // completed in every wave once all waves pass the barrier (vmcnt counts in issue order)
+      wait_vm<(NBUF - 1) * PER_CHUNK>();
+      lds_barrier();
+      if (otid() == 0) __hip_atomic_fetch_add(sig, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     bool done = false;
     for (int c = 0;; c += NBUF) {
@@ -755,6 +771,22 @@ __device__ __forceinline__ bool wg_wait(const int *p, int target, int *err, SM &
   if (otid() == 0) sm.bcast[1] = spin_geq(p, target, err) ? 1 : 0;
   __syncthreads();
   return uni(sm.bcast[1]) != 0;
+}
+
+// wg_wait for a workgroup that may hold a pending completion counter (pend, see gateup_item):
+// when the wait is not already satisfied, the pending counter is incremented first (its
+// item's stores waited for), since what this workgroup waits for may depend on it.
+template <class SM>
+__device__ __forceinline__ bool wg_wait_flush(const int *p, int target, int *err, SM &sm, int *&pend) {
+  if (pend != nullptr) {
+    __syncthreads();
+    if (otid() == 0) sm.bcast[1] = ld_relaxed(p) >= target ? 1 : 0;
+    __syncthreads();
+    if (uni(sm.bcast[1])) return true;
+    wg_signal(pend);
+    pend = nullptr;
+  }
+  return wg_wait(p, target, err, sm);
 }
 
 // Publishes the plan: n_mt + 1 goes into every copy of the plan flag once this workgroup's
@@ -1515,6 +1547,7 @@ template <class SM>
 __device__ __forceinline__ void scatter_item(const KParams &P, int c, SM &sm) {
   const int tid = otid(), k = P.k, E = P.E;
   const int t0 = c * P.tk, ntok = min(P.tk, P.T - t0);
+  if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
   for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = checked_id(ld_coh(P.ids + (size_t)t0 * k + q), E);
   __syncthreads();
   chunk_masks(P, ntok, sm);
@@ -1524,6 +1557,7 @@ __device__ __forceinline__ void scatter_item(const KParams &P, int c, SM &sm) {
     if (P.phases & PH_FFN) sm.u.r.tmp[e] = ld_coh(P.mtoff + e);
   }
   __syncthreads();
+  if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
   chunk_scatter(P, c, ntok, sm.u.r.scan0, sm.u.r.scan1, sm.u.r.tmp, sm);
 }
 
@@ -1544,9 +1578,60 @@ __device__ __forceinline__ void store4(void *base, size_t idx, f4 v) {
   }
 }
 
+// The result tile of one wave (NC fragments of 16 columns by MG groups of 16 rows; lane
+// (g, j) holds columns 16 c + 4 g .. 16 c + 4 g + 3 of row 16 b + j in v[c][b]) stored to rows
+// [0, m) of a row-major matrix in the activation dtype, through the wave's slab of LDS: each
+// row's 16 * NC values leave as one contiguous run, 16 bytes per lane per store, rather than
+// as 8-byte pieces scattered over four times as many lines.  base: the tile's first row (a
+// buffer resource: the rows' offsets from it stay below 4 GB, every one being below the
+// number of tokens times the row length), ld: row length in elements, col0: the wave's
+// first column.  Device-coherent stores (read by other workgroups in this launch).  A wave
+// reads back only what its own lanes wrote, and its LDS operations complete in order.
+template <int WT, int NC, int NFT, int MG>
+__device__ __forceinline__ void store_tile(const f4 (&v)[NFT][MG], char *slab, const void *base, int ld, int col0, int m) {
+  constexpr int ES = WT == WF32 ? 4 : 2;
+  constexpr int RB = NC * 16 * ES, RS = RB + 16, LPR = RB / 16, RPI = 64 / LPR;
+  static_assert(NC <= NFT && RPI >= 1 && 16 % RPI == 0, "tile store shape");
+  const int lane = otid() & 63, g = lane >> 4, j = lane & 15;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+  const int rr = lane / LPR, cb = (lane % LPR) * 16;
+#pragma unroll
+  for (int b = 0; b < MG; ++b) {
+    if (b * 16 >= m) break;
+#pragma unroll
+    for (int a = 0; a < NC; ++a) {
+      char *p = slab + j * RS + (16 * a + 4 * g) * ES;
+      if constexpr (ES == 4) {
+        *reinterpret_cast<f4 *>(p) = v[a][b];
+      } else {
+        const uint32_t lo = (uint32_t)f2bf(v[a][b][0]) | ((uint32_t)f2bf(v[a][b][1]) << 16);
+        const uint32_t hi = (uint32_t)f2bf(v[a][b][2]) | ((uint32_t)f2bf(v[a][b][3]) << 16);
+        *reinterpret_cast<uint2 *>(p) = make_uint2(lo, hi);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16 / RPI; ++q) {
+      const int row = q * RPI + rr;
+      const u32x4 x = *reinterpret_cast<const u32x4 *>(slab + row * RS + cb);
+      if (b * 16 + row < m)
+        __builtin_amdgcn_raw_buffer_store_b128(x, rs, (uint32_t)(((b * 16 + row) * ld + col0) * ES + cb), 0, kCpolSc1);
+    }
+  }
+}
+template <int WT, int NC, class SM>
+__device__ __forceinline__ char *store_slab(SM &sm) {
+  constexpr int ES = WT == WF32 ? 4 : 2, RS = NC * 16 * ES + 16;
+  static_assert(sizeof(sm.u) >= kWaves * 16 * RS, "tile store slabs");
+  return reinterpret_cast<char *>(&sm.u) + (otid() >> 6) * 16 * RS;
+}
+
 // gate/up item: rows (tokens) of one m-tile x gu_cols H columns; SwiGLU in registers
+// pend: the completion counter of the workgroup's previous item still to be incremented
+// (null: none); the item increments it once its own first loads are issued, and leaves its
+// own counter in pend (the caller increments it before anything waits)
 template <int WT, int MG, class SM>
-__device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i, SM &sm, const Lds3 &lb) {
+__device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i, SM &sm, const Lds3 &lb,
+                                            int *&pend) {
   using C = Core<WT, MG>;
   constexpr int NF = C::NF, NH = NF / 2;
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
@@ -1595,13 +1680,15 @@ __device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i
   f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
+  int *const sig = pend;
+  pend = nullptr;
   if constexpr (WT == WQ8) {
     // the hidden rows as E4M3 codes and block scales, written earlier in this launch
     C::template run<true, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.xq), (size_t)P.d, sm.rows, lb, P.d,
-                                  ngroups, P.xs, P.xs_stride);
+                                  ngroups, P.xs, P.xs_stride, sig);
   } else {
     C::template run<false, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.x), (size_t)P.d * asz, sm.rows,
-                                   lb, P.d, ngroups);
+                                   lb, P.d, ngroups, nullptr, 0, sig);
   }
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
   if constexpr (WT == WQ8) {
@@ -1643,30 +1730,26 @@ __device__ __forceinline__ void gateup_item(const KParams &P, bool shared, int i
     }
   } else {
 #pragma unroll
-    for (int b = 0; b < MG; ++b) {
-      const int r = b * 16 + j;
-      if (r < m) {
+    for (int b = 0; b < MG; ++b)
 #pragma unroll
-        for (int a = 0; a < NH; ++a) {
-          f4 h;
+      for (int a = 0; a < NH; ++a)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = silu_mul(acc[a][b][q], acc[a + NH][b][q]);
-          store4<WT>(P.H, (hrow0 + r) * (size_t)P.n + n0 + 16 * a + 4 * g, h);
-        }
-      }
-    }
+        for (int q = 0; q < 4; ++q) acc[a][b][q] = silu_mul(acc[a][b][q], acc[a + NH][b][q]);
+    store_tile<WT, NH>(acc, store_slab<WT, NH>(sm),
+                       reinterpret_cast<const char *>(P.H) + hrow0 * (size_t)P.n * asz, P.n, n0, m);
   }
-  wg_signal(P.gudone + counter);
+  pend = P.gudone + counter;  // (incremented once the H stores have completed)
 }
 
 // down item: rows of one m-tile x dn_cols output columns
+// (pend: as for gateup_item)
 template <int WT, int MG, class SM>
-__device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm, const Lds3 &lb) {
+__device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm, const Lds3 &lb, int *&pend) {
   using C = Core<WT, MG>;
   constexpr int NF = C::NF;
   const int tid = otid(), wv = uni(tid >> 6), lane = tid & 63, g = lane >> 4, j = lane & 15;
   const int gm = i / P.nt_dn, dt = i % P.nt_dn;
-  if (!wg_wait(P.gudone + gm, P.nt_gu, P.ctrl + kSlotInts * C_ERR, sm)) return false;
+  if (!wg_wait_flush(P.gudone + gm, P.nt_gu, P.ctrl + kSlotInts * C_ERR, sm, pend)) return false;
   const bool shared = gm < P.n_shmt;
   int e, m;
   size_t row0;
@@ -1702,25 +1785,20 @@ __device__ __forceinline__ bool down_item(const KParams &P, int i, SM &sm, const
   f4 acc[NF][MG];
   const int ngroups = (m + 15) >> 4;
   if (P.trace && tid == 0) sm.mark[0] = (uint32_t)wall_clock64();
+  int *const sig = pend;
+  pend = nullptr;
   if constexpr (WT == WQ8)  // H as E4M3 codes (one byte per value) and block scales
     C::template run<true, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n, sm.rows, lb, P.n,
-                                  ngroups, P.hs, P.hs_stride);
+                                  ngroups, P.hs, P.hs_stride, sig);
   else
     C::template run<true, kWStep>(acc, wrow, sc, reinterpret_cast<const char *>(P.H), (size_t)P.n * asz, sm.rows, lb,
-                                  P.n, ngroups);
+                                  P.n, ngroups, nullptr, 0, sig);
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
-#pragma unroll
-  for (int b = 0; b < MG; ++b) {
-    const int r = b * 16 + j;
-    if (r < m) {
-#pragma unroll
-      for (int a = 0; a < NF; ++a) {
-        const int c = d0 + 16 * a + 4 * g;
-        if (c < P.d) store4<WT>(P.Y, (row0 + r) * (size_t)P.d + c, acc[a][b]);
-      }
-    }
-  }
-  wg_signal(P.dndone + gm);
+  // (d is a multiple of 256, the columns of a down item: every wave's columns exist)
+  const size_t ysz = WT == WF32 ? 4 : 2;  // Y in the activation dtype (bf16 also with fp8 activations)
+  store_tile<WT, NF>(acc, store_slab<WT, NF>(sm), reinterpret_cast<const char *>(P.Y) + row0 * (size_t)P.d * ysz,
+                     P.d, d0, m);
+  pend = P.dndone + gm;  // (incremented once the Y stores have completed)
   return true;
 }
 
@@ -2088,7 +2166,8 @@ void moe_persistent(KParams P) {
   }
   const int n_Z = P.n_Z, n_L = P.n_L, n_K = P.n_K, n_SG = P.n_SG, n_S = P.n_S;
   const int n_Q = WT == WQ8 ? P.n_Q : 0;
-  const int n_bound = n_Z + n_L + n_Q;  // items before the first ticketed one (trace numbering)
+  const int n_bound = n_Z + n_L;  // items before the first ticketed one (trace numbering)
+  const int n_early = n_K + n_SG + n_S + n_Q;  // ticketed items before the gate/up, down, combine items
   const bool dyn = (P.phases & (PH_FFN | PH_COMBINE)) != 0;
   bool zero_seen = false, logits_seen = false, scat_seen = false, comb_scat_seen = false;
   bool quant_seen = WT != WQ8;
@@ -2096,6 +2175,17 @@ void moe_persistent(KParams P) {
   const int n_S_comb = n_S + ((P.n_kc <= 1 && (P.phases & PH_PERMUTE)) ? 1 : 0);
   int n_mt = -1;
   int step = 0;
+  // The completion counter of the last gate/up or down item of this workgroup (m-tiles above
+  // 16 rows), incremented once its result stores complete: by the next item after its first
+  // loads are issued (the stores drain while they are in flight), or here before anything
+  // waits or the workgroup exits (what it waits for may depend on that counter).
+  int *pend = nullptr;
+  auto flush = [&]() {
+    if (pend != nullptr) {
+      wg_signal(pend);
+      pend = nullptr;
+    }
+  };
   const bool dynamic = P.schedule == 0;
   // Dynamic tickets come from np = min(kTicketParts, grid) counters, one per partition of
   // the workgroups: partition p hands out the tickets p, p + np, ... in order.  Workgroup b
@@ -2140,9 +2230,16 @@ void moe_persistent(KParams P) {
     wg_signal(ctrl + kSlotInts * C_LDONE);
     record(n_Z + r, K_ROUTER, t_start);
   }
+  // The first ticket is taken here, before the counter-clearing items, so that every
+  // workgroup holds one top-k ticket before any workgroup takes a second ticket (a top-k
+  // item behind another one on the same workgroup would delay the plan by a whole item).
+  bool have_next = false;  // (thread 0) `next` holds a fetched ticket
+  if (dynamic && tid == 0) {
+    next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    have_next = true;
+  }
   // The counter-clearing items take no ticket either: workgroup grid - 1 - b runs items b,
-  // b + grid, ... (the last workgroups, which have router items only when every one has),
-  // so that every top-k item finds a workgroup in the first round of tickets.
+  // b + grid, ... (the last workgroups, which have router items only when every one has).
   for (int z = (int)gridDim.x - 1 - (int)blockIdx.x; z < n_Z; z += (int)gridDim.x) {
     __syncthreads();
     const uint64_t t_start = P.trace ? wall_clock64() : 0;
@@ -2151,23 +2248,6 @@ void moe_persistent(KParams P) {
     wg_signal(ctrl + kSlotInts * C_ZDONE);
     record(z, K_ZERO, t_start);
   }
-  // Activation-quantisation items (fp8 activations) take no ticket either: workgroup b runs
-  // items b - n_L, b - n_L + grid, ... (mod grid: the workgroups after the router items' first
-  // round start on them).  They wait for nothing; the gate/up items wait for all of them.
-  if constexpr (WT == WQ8) {
-    const int G = (int)gridDim.x;
-    for (int q = (((int)blockIdx.x - n_L) % G + G) % G; q < n_Q; q += G) {
-      __syncthreads();
-      const uint64_t t_start = P.trace ? wall_clock64() : 0;
-      if (P.trace && tid == 0) sm.mark[0] = sm.mark[1] = 0;
-      quant_item(P, q);
-      wg_signal(ctrl + kSlotInts * C_QDONE);
-      record(n_Z + n_L + q, K_QUANT, t_start);
-    }
-  }
-  // (the first ticket is taken after these items, so the first tickets go to workgroups
-  // that are free)
-  if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // Late phase (m-tiles of more than 16 rows, dynamic schedule).  The gate/up and down items
   // are split over one queue per XCD: the m-tiles u (the shared expert's first, then the
   // routed ones, in expert order) form contiguous ranges, XCD x holding [x U / 8, (x+1) U / 8)
@@ -2193,14 +2273,23 @@ void moe_persistent(KParams P) {
     int phase = -1, idx = 0, item = 0;
     if (stage == 0) {
       if (dynamic) {
-        if (tid == 0) sm.bcast[0] = part + nparts * next;
+        if (tid == 0) {
+          if (!have_next) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sm.bcast[0] = part + nparts * next;
+        }
         __syncthreads();
       }
       const int ticket = dynamic ? uni(sm.bcast[0]) : (int)blockIdx.x + step * (int)gridDim.x;
       ++step;
-      // prefetch the next ticket; its value is read at the top of the next iteration
-      if (dynamic && tid == 0) next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      item = ticket + n_bound;  // (counter-clearing, router and quantisation items are not ticketed)
+      // prefetch the next ticket (its value is read at the top of the next iteration), except
+      // during a top-k item: a second ticket taken then could be another top-k item, which
+      // this workgroup would start only after the current one
+      have_next = false;
+      if (dynamic && tid == 0 && ticket >= n_K) {
+        next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        have_next = true;
+      }
+      item = ticket + n_bound;  // (counter-clearing and router items are not ticketed)
       int i = ticket;
       if (i < n_K) {
         phase = 0, idx = i;
@@ -2208,14 +2297,17 @@ void moe_persistent(KParams P) {
         phase = 1, idx = i;
       } else if ((i -= n_SG) < n_S) {
         phase = 2, idx = i;
+      } else if ((i -= n_S) < n_Q) {
+        phase = 6, idx = i;
       } else {
-        i -= n_S;
+        i -= n_Q;
         if (!dyn) break;
         if (MG > 1 && P.late) {  // (16-row m-tiles never use the late phase)
           held = ticket;
           stage = 1;
           continue;
         }
+        if (n_mt < 0) flush();
         if (n_mt < 0 && (n_mt = wg_wait_plan(P, sm)) < 0) break;
         const int n_G = n_mt * P.nt_gu;
         const int n_D = (n_mt + P.n_shmt) * P.nt_dn;
@@ -2225,6 +2317,7 @@ void moe_persistent(KParams P) {
         else break;
       }
     } else if (MG > 1 && stage == 1) {
+      if (n_mt < 0) flush();
       if (n_mt < 0 && (n_mt = wg_wait_plan(P, sm)) < 0) break;
       const int U = P.n_shmt + n_mt;
       if (xq < 0) {  // first late item of this workgroup: its XCD's queue
@@ -2257,7 +2350,6 @@ void moe_persistent(KParams P) {
       const int ntile = gu ? P.nt_gu : P.nt_dn, per = P.group_m * ntile;
       const int grp = q / per, r = q - grp * per, u0 = lo + grp * P.group_m, gs = min(P.group_m, hi - u0);
       const int j = r / gs, u = u0 + (r - j * gs);
-      const int n_early = n_K + n_SG + n_S;
       if (!gu) {
         phase = 4, idx = u * P.nt_dn + j;
         item = n_bound + n_early + U * P.nt_gu + idx;
@@ -2268,7 +2360,6 @@ void moe_persistent(KParams P) {
       }
     } else if (MG > 1) {
       // combine items: this workgroup's early tickets from `held` on, item = ticket - n_early
-      const int n_early = n_K + n_SG + n_S;
       const int c = held - n_early;
       if (c >= P.n_comb) break;
       if (tid == 0) {
@@ -2288,10 +2379,12 @@ void moe_persistent(KParams P) {
     const int i = idx;
     if (phase == 0) {
       if (!(P.phases & PH_IDS_GIVEN) && !logits_seen) {
+        flush();
         if (!wg_wait(ctrl + kSlotInts * C_LDONE, n_L, err, sm)) break;
         logits_seen = true;
       }
       if (!zero_seen && P.n_kc > 1) {  // chunk histograms are cleared by the Z items
+        flush();
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
       }
@@ -2299,47 +2392,59 @@ void moe_persistent(KParams P) {
       kind = K_TOPK;
     } else if (phase == 1) {
       if (!zero_seen) {
+        flush();
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
       }
       if (!quant_seen) {  // the quantised hidden rows
+        flush();
         if (!wg_wait(ctrl + kSlotInts * C_QDONE, n_Q, err, sm)) break;
         quant_seen = true;
       }
       if constexpr (MG == 1) gateup_unit<WT>(P, true, i, sm, 2 * n_SG <= kWaves * (int)gridDim.x);
-      else gateup_item<WT, MG>(P, true, i, sm, lb);
+      else gateup_item<WT, MG>(P, true, i, sm, lb, pend);
       kind = K_SHGU;
     } else if (phase == 2) {
+      flush();
       if (n_mt < 0 && (n_mt = wg_wait_plan(P, sm)) < 0) break;
       scatter_item(P, i, sm);
       wg_signal(ctrl + kSlotInts * C_SDONE);
       kind = K_SCATTER;
+    } else if (phase == 6) {
+      if constexpr (WT == WQ8) {
+        quant_item(P, i);
+        wg_signal(ctrl + kSlotInts * C_QDONE);
+      }
+      kind = K_QUANT;
     } else if (phase == 3 || phase == 4) {
       // small-tile units: a deep prefetch (8 steps) when the units are too few to keep the
       // memory system busy, else a shallow one (4 steps): with every wave of the grid
       // streaming, more requests in flight only add contention
       const bool deep = 2 * n_mt * P.nt_gu <= kWaves * (int)gridDim.x;
       if (!scat_seen) {
+        flush();
         if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S, err, sm)) break;
         scat_seen = true;
       }
       if (!zero_seen) {  // the dependency counters must be cleared before they are used
+        flush();
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
       }
       if (phase == 3 && !quant_seen) {  // the quantised hidden rows
+        flush();
         if (!wg_wait(ctrl + kSlotInts * C_QDONE, n_Q, err, sm)) break;
         quant_seen = true;
       }
       if (phase == 3) {
         if constexpr (MG == 1) gateup_unit<WT>(P, false, i, sm, deep);
-        else gateup_item<WT, MG>(P, false, i, sm, lb);
+        else gateup_item<WT, MG>(P, false, i, sm, lb, pend);
         kind = K_GU;
       } else {
         if constexpr (MG == 1) {
           if (!down_unit<WT>(P, i, sm, deep)) break;
         } else {
-          if (!down_item<WT, MG>(P, i, sm, lb)) break;
+          if (!down_item<WT, MG>(P, i, sm, lb, pend)) break;
         }
         kind = K_DN;
       }
@@ -2347,13 +2452,16 @@ void moe_persistent(KParams P) {
       // the token's rows of Y are final once the down items of their m-tiles are done (the
       // slot m-tiles come from the scatter; the counters are valid once cleared)
       if (!comb_scat_seen) {
+        flush();
         if (!wg_wait(ctrl + kSlotInts * C_SDONE, n_S_comb, err, sm)) break;
         comb_scat_seen = true;
       }
       if (!zero_seen) {
+        flush();
         if (!wg_wait(ctrl + kSlotInts * C_ZDONE, n_Z, err, sm)) break;
         zero_seen = true;
       }
+      flush();
       if (!combine_item<WT>(P, i, sm)) break;
       kind = K_COMB;
     }
@@ -2364,6 +2472,7 @@ void moe_persistent(KParams P) {
   // all returned, a relaxed increment of the exit counter orders them before the reset.  No
   // acquire or release here: at agent scope those write back and invalidate the XCD's whole
   // L2, and with every workgroup leaving at the end that would stall the items still running.
+  flush();
   __syncthreads();
   if (tid == 0) {
     wait_vm0();

@@ -2037,21 +2037,29 @@ __device__ __forceinline__ bool combine_ready(const KParams &P, int c, SM &sm) {
 }
 
 // combine: out[t] = sum_j w[t,j] * Y[inv_perm[t*k+j]] (+ Y[T*k + t]), float32, slot order.
-// It ends the layer, so latency matters: each thread keeps kCombineUnroll (token, column)
-// pairs in flight, and takes the slots 8 at a time, with all of their weights and row
-// indices loaded before all 8 rows of Y.  The first batch of weights and row indices is
-// loaded before the wait for the down items (they are final once the scatter is done).
+// It ends the layer, so latency matters.  The item's gate weights and Y row indices (final
+// once the scatter is done) are staged in LDS while it waits for the down items; then each
+// thread takes UN (token, column) pairs at a time and issues the loads of all their Y rows,
+// 8 slots per batch (and the shared expert's row with the last batch), before adding any.
 // False on timeout or fault.
-template <int WT, class SM>
+template <int WT, int UN, class SM>
 __device__ __forceinline__ bool combine_item(const KParams &P, int c, SM &sm) {
   using A = typename ActT<WT>::type;
   constexpr int VEC = 16 / sizeof(A);
   constexpr int SB = 8;  // slots per batch
-  constexpr int UN = kCombineUnroll;
+  const int tid = otid();
   const int t0 = c * P.ctok, ntok = min(P.ctok, P.T - t0);
-  const int nv = P.d / VEC, k = P.k, npair = ntok * nv;
+  const int nv = P.d / VEC, k = P.k, npair = ntok * nv, nsl = ntok * k;
   const A *Y = reinterpret_cast<const A *>(P.Y);
   A *out = reinterpret_cast<A *>(P.out);
+  static_assert(sizeof(sm.u) >= 8 * kMaxCombineSlots, "combine tables");
+  float *sw = reinterpret_cast<float *>(&sm.u);
+  int *sp = reinterpret_cast<int *>(sw + kMaxCombineSlots);
+  for (int q = tid; q < nsl; q += kThreads) {
+    sw[q] = ld_coh(P.wts + (size_t)t0 * k + q);
+    sp[q] = min(max(ld_coh(P.inv_perm + (size_t)t0 * k + q), 0), P.T * k - 1);
+  }
+  if (!combine_ready(P, c, sm)) return false;  // (its barriers also publish the tables)
   auto add = [&](float (&acc)[VEC], const uint4 &raw, float w) {
     if constexpr (WT == WF32) {
       const float *f = reinterpret_cast<const float *>(&raw);
@@ -2063,56 +2071,46 @@ __device__ __forceinline__ bool combine_item(const KParams &P, int c, SM &sm) {
       for (int z = 0; z < VEC; ++z) acc[z] += w * bf2f(h[z]);
     }
   };
-  float w[UN][SB];
-  int p[UN][SB];
-  auto load_wp = [&](const int (&t)[UN], int j0) {
-#pragma unroll
-    for (int x = 0; x < UN; ++x)
-#pragma unroll
-      for (int b = 0; b < SB; ++b) {
-        const size_t at = (size_t)t[x] * k + min(j0 + b, k - 1);
-        w[x][b] = ld_coh(P.wts + at);
-        p[x][b] = ld_coh(P.inv_perm + at);
-      }
-  };
-  {
-    int t[UN];
-#pragma unroll
-    for (int x = 0; x < UN; ++x) t[x] = t0 + min(otid() + x * kThreads, max(npair - 1, 0)) / max(nv, 1);
-    load_wp(t, 0);
-  }
-  if (!combine_ready(P, c, sm)) return false;
-  bool first = true;
-  for (int q0 = otid(); q0 < npair; q0 += UN * kThreads) {
-    int t[UN], v[UN];
+  for (int q0 = tid; q0 < npair; q0 += UN * kThreads) {
+    int tl[UN], v[UN];
     float acc[UN][VEC];
 #pragma unroll
     for (int x = 0; x < UN; ++x) {
       const int q = min(q0 + x * kThreads, npair - 1);  // (clamped: repeats a valid pair)
-      t[x] = t0 + q / nv;
+      tl[x] = q / nv;
       v[x] = q % nv;
 #pragma unroll
       for (int z = 0; z < VEC; ++z) acc[x][z] = 0.f;
     }
     for (int j0 = 0; j0 < k; j0 += SB) {
-      if (!first) load_wp(t, j0);
-      first = false;
-      uint4 raw[UN][SB];
+      const bool last = j0 + SB >= k;
+      uint4 raw[UN][SB], sh[UN];
+      float w[UN][SB];
 #pragma unroll
       for (int x = 0; x < UN; ++x)
 #pragma unroll
-        for (int b = 0; b < SB; ++b)
-          raw[x][b] = ld_coh16(Y + (size_t)min(max(p[x][b], 0), P.T * k - 1) * P.d + v[x] * VEC);
+        for (int b = 0; b < SB; ++b) {
+          const int sl = tl[x] * k + min(j0 + b, k - 1);
+          w[x][b] = sw[sl];
+          raw[x][b] = ld_coh16(Y + (size_t)sp[sl] * P.d + v[x] * VEC);
+        }
+      if (P.S && last) {
+#pragma unroll
+        for (int x = 0; x < UN; ++x) sh[x] = ld_coh16(Y + ((size_t)P.T * k + t0 + tl[x]) * P.d + v[x] * VEC);
+      }
 #pragma unroll
       for (int x = 0; x < UN; ++x)
 #pragma unroll
         for (int b = 0; b < SB; ++b)
           if (j0 + b < k) add(acc[x], raw[x][b], w[x][b]);
+      if (P.S && last) {
+#pragma unroll
+        for (int x = 0; x < UN; ++x) add(acc[x], sh[x], 1.0f);
+      }
     }
 #pragma unroll
     for (int x = 0; x < UN; ++x) {
       if (q0 + x * kThreads >= npair) continue;
-      if (P.S) add(acc[x], ld_coh16(Y + ((size_t)P.T * k + t[x]) * P.d + v[x] * VEC), 1.0f);
       uint4 o;
       if constexpr (WT == WF32) {
         o = make_uint4(__float_as_uint(acc[x][0]), __float_as_uint(acc[x][1]), __float_as_uint(acc[x][2]),
@@ -2123,7 +2121,7 @@ __device__ __forceinline__ bool combine_item(const KParams &P, int c, SM &sm) {
         for (int z = 0; z < 4; ++z) wv[z] = (uint32_t)f2bf(acc[x][2 * z]) | ((uint32_t)f2bf(acc[x][2 * z + 1]) << 16);
         o = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
-      *reinterpret_cast<uint4 *>(out + (size_t)t[x] * P.d + v[x] * VEC) = o;
+      *reinterpret_cast<uint4 *>(out + (size_t)(t0 + tl[x]) * P.d + v[x] * VEC) = o;
     }
   }
   return true;
@@ -2462,7 +2460,7 @@ void moe_persistent(KParams P) {
         zero_seen = true;
       }
       flush();
-      if (!combine_item<WT>(P, i, sm)) break;
+      if (!combine_item<WT, Occ<WT, MG>::waves == 1 ? 4 : kCombineUnroll>(P, i, sm)) break;
       kind = K_COMB;
     }
     record(item, kind, t_start);

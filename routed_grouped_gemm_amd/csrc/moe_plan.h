@@ -41,6 +41,8 @@ constexpr int router_groups(int mg) { return mg >= 8 ? 4 : 1; }
 constexpr int kMaxChunkTokens = 128;   // tokens per scatter chunk (rank bitmasks: 4 words)
 constexpr int kMaxChunkSlots = 1024;   // (token, slot) pairs per chunk
 constexpr int kCombineUnroll = 2;      // combine: (token, column) pairs per thread in flight
+constexpr int kMaxCombineTokens = 4;   // tokens per combine item (Tiles::ctok) at most
+constexpr int kMaxCombineSlots = kMaxCombineTokens * kMaxK;  // (token, slot) pairs per combine item
 constexpr int kZeroPerItem = 2048;     // dependency counters cleared per zeroing item
 constexpr int kQuantTokens = 16;       // tokens per activation-quantisation item (fp8 activations)
 
@@ -150,7 +152,7 @@ inline Tiles tiles_for(const moe_problem *p, int mg, int group_m) {
   t.tk = kMaxChunkSlots / p->k;
   if (t.tk > kMaxChunkTokens) t.tk = kMaxChunkTokens;
   if (t.tk < 1) t.tk = 1;
-  t.ctok = p->T > 1024 ? 4 : 1;
+  t.ctok = p->T > 1024 ? kMaxCombineTokens : 1;
   t.late = t.mg > 1 ? 1 : 0;
   t.group_m = group_m;
   t.aq = (p->act_quant == MOE_AQ_FP8 && t.mg > 1) ? 1 : 0;

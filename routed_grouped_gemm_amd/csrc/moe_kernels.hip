@@ -466,13 +466,27 @@ template <int WT, int MG> struct Core {
       Bop bv[LA];
 #pragma unroll
       for (int t = 0; t < LA; ++t) bv[t] = rd(t);
+      f4 prev;  // the last product not yet scaled into its accumulators
 #pragma unroll
       for (int b = 0; b < MG; ++b) {
         const Bop cur = bv[b % LA];
         if (b + LA < MG) bv[b % LA] = rd(b + LA);
         if (FULL || b == 0 || b < ngroups) {
+          // each product is scaled into its accumulators after the next MFMA is issued, so
+          // that the vector FMAs overlap an MFMA instead of waiting for their own (with one
+          // result register for every product, each MFMA would wait for the previous FMAs);
+          // the present groups are a prefix, so group b - 1's last product is still pending
+          // here unless b is the first group, and the last present group scales its own
+          f4 r = mfma_fp8x8(W[0][0], W[0][1], cur.lo, cur.hi, cur.s);
+          if (b > 0) acc[NF - 1][b - 1] += prev * sw[NF - 1];
+          prev = r;
 #pragma unroll
-          for (int a = 0; a < NF; ++a) acc[a][b] += mfma_fp8x8(W[a][0], W[a][1], cur.lo, cur.hi, cur.s) * sw[a];
+          for (int a = 1; a < NF; ++a) {
+            r = mfma_fp8x8(W[a][0], W[a][1], cur.lo, cur.hi, cur.s);
+            acc[a - 1][b] += prev * sw[a - 1];
+            prev = r;
+          }
+          if (b + 1 == MG || !(FULL || b + 1 < ngroups)) acc[NF - 1][b] += prev * sw[NF - 1];
         }
       }
     } else if constexpr (WT == WFP8 && MG >= MOE_FP8_FOLD_MG) {
@@ -680,7 +694,10 @@ template <int WT, int MG> struct Core {
     // which also keeps the compiler from hoisting every LDS read of the chunk at once
     auto compute = [&](const uint4(&W)[NF][FL], const char *A, int c) {
       asm volatile("" ::: "memory");  // the stage's prefetches are issued before its math
-      chunk_mfma<(MG <= 2)>(acc, W, A, sc, c, ngroups, g, j, lb.sl, sstride);
+#ifndef MOE_FULL_MASK
+#define MOE_FULL_MASK (1 << WQ8)
+#endif
+      chunk_mfma<(MG <= 2) || ((MOE_FULL_MASK >> WT) & 1)>(acc, W, A, sc, c, ngroups, g, j, lb.sl, sstride);
     };
     // NBUF register/LDS stages, NBUF - 1 chunks in flight: each step waits only for its own
     // chunk (vmcnt counts this wave's outstanding operations, which complete in issue order,

@@ -494,18 +494,20 @@ template <int WT, int MG> struct Core {
       // each fragment has one block scale per 128-wide K block; its codes are decoded, multiplied
       // by that scale and rounded to bf16 once per chunk, shared by the MG token groups, and the
       // MFMAs accumulate straight into acc (no per-block partial sums to scale)
-      constexpr int BPC = FL / 2;  // 128-wide scale blocks per chunk (a step is 64 codes)
+      // (FL == 1: a chunk is half of a 128-wide scale block, chunk c in block c / 2)
+      constexpr int SPB = FL < 2 ? 1 : 2;  // steps per scale block within a chunk
+      constexpr int BPC = FL / SPB;        // scale blocks per chunk (a step is 64 codes)
       bf16x8 D[NF][FL][2];
 #pragma unroll
       for (int blk = 0; blk < BPC; ++blk) {
 #pragma unroll
         for (int a = 0; a < NF; ++a) {
-          const float s = ld_uniform(sc[a] + c * BPC + blk);
+          const float s = ld_uniform(sc[a] + (FL < 2 ? (c >> 1) : c * BPC + blk));
 #pragma unroll
-          for (int ff = 0; ff < 2; ++ff) {
-            const uint4 &w = W[a][blk * 2 + ff];
-            D[a][blk * 2 + ff][0] = fp8x8_to_bf16_scaled(w.x, w.y, s);
-            D[a][blk * 2 + ff][1] = fp8x8_to_bf16_scaled(w.z, w.w, s);
+          for (int ff = 0; ff < SPB; ++ff) {
+            const uint4 &w = W[a][blk * SPB + ff];
+            D[a][blk * SPB + ff][0] = fp8x8_to_bf16_scaled(w.x, w.y, s);
+            D[a][blk * SPB + ff][1] = fp8x8_to_bf16_scaled(w.z, w.w, s);
           }
         }
       }

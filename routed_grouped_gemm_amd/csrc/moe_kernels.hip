@@ -421,6 +421,10 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, in
 // 64-byte step f of the row, and the activation operand of token (16*mg + j) over the
 // same K positions; result D[4*g + r][j] = channel (frag base + 4*g + r), token 16*mg + j.
 // ---------------------------------------------------------------------------------
+// Branch-free token groups: the small tiles and the fp8-activation tiles (their block-scaled
+// products then pipeline with the MFMAs; 20 % faster).  The larger bf16, fp32 and w8a16 tiles
+// skip absent groups (computing them cost more on partly filled m-tiles: skewed layer 829 ->
+// 972 us with every group computed).
 template <int WT, int MG> struct Core {
   static constexpr int NF = Shape<WT, MG>::NF, FL = Shape<WT, MG>::FL;
   static constexpr int KU = Ty<WT>::KU, ASZ = Ty<WT>::ASZ;
@@ -691,15 +695,13 @@ template <int WT, int MG> struct Core {
         for (int a = 0; a < NF; ++a)
           W[a][f] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc[a], woff[a], off + f * WSTEP, wpol));
     };
-    // small tiles compute every token group (rows past the tile's end repeat its last
-    // row, valid data whose results are not stored); large tiles skip absent groups,
-    // which also keeps the compiler from hoisting every LDS read of the chunk at once
+    // small tiles and the fp8-activation tiles compute every token group (rows past the
+    // tile's end repeat its last row, valid data whose results are not stored); the other
+    // large tiles skip absent groups, which also keeps the compiler from hoisting every LDS
+    // read of the chunk at once
     auto compute = [&](const uint4(&W)[NF][FL], const char *A, int c) {
       asm volatile("" ::: "memory");  // the stage's prefetches are issued before its math
-#ifndef MOE_FULL_MASK
-#define MOE_FULL_MASK (1 << WQ8)
-#endif
-      chunk_mfma<(MG <= 2) || ((MOE_FULL_MASK >> WT) & 1)>(acc, W, A, sc, c, ngroups, g, j, lb.sl, sstride);
+      chunk_mfma<(MG <= 2) || WT == WQ8>(acc, W, A, sc, c, ngroups, g, j, lb.sl, sstride);
     };
     // NBUF register/LDS stages, NBUF - 1 chunks in flight: each step waits only for its own
     // chunk (vmcnt counts this wave's outstanding operations, which complete in issue order,
@@ -1019,7 +1021,11 @@ __device__ __forceinline__ void logits_item_tile(const KParams &P, int i, SM &sm
     for (int z = 0; z < 4; ++z) bv[z] = e + z < P.E ? P.bias[e + z] : 0.f;
   }
   float *const dst = S == 1 ? P.logits : P.lpart + (size_t)ks * P.T * P.E;
-  const bool vec = e + 3 < P.E && (P.E & 1) == 0;  // 8-byte aligned pairs, all four in range
+  // four consecutive logits of a token as one 16-byte device-coherent store (a buffer
+  // resource at the tile's first token row: the tile's rows span at most 64 rows of E floats)
+  // when all four are in range and 16-byte aligned, else one by one
+  const bool vec = e + 3 < P.E && (P.E & 3) == 0;
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(dst + (size_t)t0 * P.E);
 #pragma unroll
   for (int b = 0; b < RMG; ++b) {
     if (b * 16 >= m) break;
@@ -1032,8 +1038,9 @@ __device__ __forceinline__ void logits_item_tile(const KParams &P, int i, SM &sm
       if (b * 16 + row >= m || e >= P.E) continue;
       float *p = dst + (size_t)(t0 + b * 16 + row) * P.E + e;
       if (vec) {
-        st_coh64(p, (uint64_t)__float_as_uint(v[0] + bv[0]) | ((uint64_t)__float_as_uint(v[1] + bv[1]) << 32));
-        st_coh64(p + 2, (uint64_t)__float_as_uint(v[2] + bv[2]) | ((uint64_t)__float_as_uint(v[3] + bv[3]) << 32));
+        const u32x4 q = {__float_as_uint(v[0] + bv[0]), __float_as_uint(v[1] + bv[1]), __float_as_uint(v[2] + bv[2]),
+                         __float_as_uint(v[3] + bv[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(q, lrs, (uint32_t)(((b * 16 + row) * P.E + e) * 4), 0, kCpolSc1);
       } else {
 #pragma unroll
         for (int z = 0; z < 4; ++z)
@@ -1297,7 +1304,10 @@ __device__ __forceinline__ void topk_group(const KParams &P, const int (&t)[TPW]
 // winner.  Several tied lanes take the lowest id among their heads (wave max of the
 // complemented ids).  The winning lane drops its head.  Slot j's id and logit land in
 // lane j (k <= 64); for k > 64 lane 0 also writes the ids to LDS.
-template <int TPW>
+// V4: lane l holds experts 4 l .. 4 l + 3 (key q is expert 4 l + q), else experts l, l + 64,
+// l + 128, l + 192 (key q is expert 64 q + l); either way a lane's keys start in increasing
+// expert order, which the stable sort keeps for equal keys
+template <int TPW, bool V4>
 __device__ __forceinline__ void topk_group4(const KParams &P, const int (&t)[TPW], const bool (&live)[TPW],
                                             uint32_t (&key)[TPW][4], int16_t *const (&ids_lds)[TPW]) {
   const int lane = otid() & 63, k = P.k;
@@ -1345,7 +1355,8 @@ __device__ __forceinline__ void topk_group4(const KParams &P, const int (&t)[TPW
     if (many) {
       uint32_t c[TPW];
 #pragma unroll
-      for (int u = 0; u < TPW; ++u) c[u] = key[u][0] == m[u] ? ~(uint32_t)(qq[u][0] * 64 + lane) : 0u;
+      for (int u = 0; u < TPW; ++u)
+        c[u] = key[u][0] == m[u] ? ~(uint32_t)(V4 ? lane * 4 + qq[u][0] : qq[u][0] * 64 + lane) : 0u;
       wave_max_u32<TPW>(c);
 #pragma unroll
       for (int u = 0; u < TPW; ++u) win[u] = (int)~c[u];
@@ -1353,12 +1364,13 @@ __device__ __forceinline__ void topk_group4(const KParams &P, const int (&t)[TPW
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const int wl = (int)__builtin_ctzll(tie[u]);
-        win[u] = __builtin_amdgcn_readlane(qq[u][0], wl) * 64 + wl;
+        const int wq = __builtin_amdgcn_readlane(qq[u][0], wl);
+        win[u] = V4 ? wl * 4 + wq : wq * 64 + wl;
       }
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      const bool pop = lane == (win[u] & 63);
+      const bool pop = lane == (V4 ? win[u] >> 2 : win[u] & 63);
       key[u][0] = pop ? key[u][1] : key[u][0];
       key[u][1] = pop ? key[u][2] : key[u][1];
       key[u][2] = pop ? key[u][3] : key[u][2];
@@ -1390,9 +1402,18 @@ __device__ __forceinline__ void topk_group4(const KParams &P, const int (&t)[TPW
 // loads are unconditional (clamped index, masked after): a load under a lane condition is
 // waited for inside its branch, which would serialise the loads.
 // SMAX: the most parts the router's K can be split into in this kernel
-template <int TPW, int SMAX, class SM>
+// V4 (E a multiple of 4): a lane holds 4 consecutive experts' logits, read as one 16-byte
+// load per token and K part (else 4 loads 64 experts apart)
+template <int TPW, int SMAX, bool V4, class SM>
 __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, SM &sm) {
   const int tid = otid(), wave = tid >> 6, lane = tid & 63, k = P.k, E = P.E;
+  auto eid = [&](int q) { return V4 ? lane * 4 + q : q * 64 + lane; };
+  // 16-byte device-coherent load of 4 logits of a row (row: wave-uniform); lanes past E read
+  // the row's last 4 (their keys are dropped)
+  auto ld4 = [&](const float *row) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(uni64(reinterpret_cast<uint64_t>(row))));
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(min(lane * 4, E - 4) * 4), 0, kCpolSc1));
+  };
   if (E <= 256) {
     float v[TPW][4];
     int t[TPW];
@@ -1413,8 +1434,14 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const float *Lr = L0 + (size_t)t[u] * E;
+      if constexpr (V4) {
+        const f4 r = ld4(Lr);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[u][q] = ld_coh(Lr + min(q * 64 + lane, E - 1));
+        for (int q = 0; q < 4; ++q) v[u][q] = r[q];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[u][q] = ld_coh(Lr + min(eid(q), E - 1));
+      }
     }
     asm volatile("" ::: "memory");  // all of the wave's loads are in flight before any is used
     if (S > 1) {
@@ -1423,10 +1450,17 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
 #pragma unroll
       for (int u = 0; u < TPW; ++u)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int x = 0; x < SMAX - 1; ++x) {
+          const float *Lp = P.lpart + ((size_t)min(x + 1, S - 1) * P.T + t[u]) * E;
+          if constexpr (V4) {
+            const f4 r = ld4(Lp);
 #pragma unroll
-          for (int x = 0; x < SMAX - 1; ++x)
-            pp[u][q][x] = ld_coh(P.lpart + ((size_t)min(x + 1, S - 1) * P.T + t[u]) * E + min(q * 64 + lane, E - 1));
+            for (int q = 0; q < 4; ++q) pp[u][q][x] = r[q];
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pp[u][q][x] = ld_coh(Lp + min(eid(q), E - 1));
+          }
+        }
 #pragma unroll
       for (int u = 0; u < TPW; ++u)
 #pragma unroll
@@ -1436,11 +1470,25 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
             if (x + 1 < S) v[u][q] += pp[u][q][x];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float bq = P.bias ? P.bias[min(q * 64 + lane, E - 1)] : 0.f;
+        const float bq = P.bias ? P.bias[min(eid(q), E - 1)] : 0.f;
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          v[u][q] += bq;
-          if (live[u] && q * 64 + lane < E) st_coh(P.logits + (size_t)t[u] * E + q * 64 + lane, v[u][q]);
+        for (int u = 0; u < TPW; ++u) v[u][q] += bq;
+      }
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        if (!live[u]) continue;
+        float *Lo = P.logits + (size_t)t[u] * E;
+        if constexpr (V4) {
+          if (lane * 4 < E) {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(uni64(reinterpret_cast<uint64_t>(Lo))));
+            const u32x4 o = {__float_as_uint(v[u][0]), __float_as_uint(v[u][1]), __float_as_uint(v[u][2]),
+                             __float_as_uint(v[u][3])};
+            __builtin_amdgcn_raw_buffer_store_b128(o, rs, (uint32_t)(lane * 16), 0, kCpolSc1);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (eid(q) < E) st_coh(Lo + eid(q), v[u][q]);
         }
       }
     }
@@ -1448,8 +1496,8 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) key[u][q] = (q * 64 + lane < E) ? ordered_key(v[u][q]) : 0u;
-    topk_group4<TPW>(P, t, live, key, ids);
+      for (int q = 0; q < 4; ++q) key[u][q] = (eid(q) < E) ? ordered_key(v[u][q]) : 0u;
+    topk_group4<TPW, V4>(P, t, live, key, ids);
   } else {
     for (int tt = wave; tt < ntok; tt += kWaves) {
       const int t[1] = {t0 + tt};
@@ -1483,9 +1531,10 @@ __device__ __forceinline__ void topk_tokens(const KParams &P, int t0, int ntok, 
 // holds a slot of the wave's limited count of outstanding memory operations)
 template <int TPW, int SMAX, class SM>
 __device__ __forceinline__ void topk_tokens_parts(const KParams &P, int t0, int ntok, SM &sm) {
-  if (P.rt_split <= 2 || SMAX <= 2) topk_tokens<TPW, (SMAX < 2 ? SMAX : 2)>(P, t0, ntok, sm);
-  else if (P.rt_split <= 4 || SMAX <= 4) topk_tokens<TPW, (SMAX < 4 ? SMAX : 4)>(P, t0, ntok, sm);
-  else topk_tokens<TPW, SMAX>(P, t0, ntok, sm);
+  if ((P.E & 3) != 0) topk_tokens<TPW, SMAX, false>(P, t0, ntok, sm);  // (rare: E not a multiple of 4)
+  else if (P.rt_split <= 2 || SMAX <= 2) topk_tokens<TPW, (SMAX < 2 ? SMAX : 2), true>(P, t0, ntok, sm);
+  else if (P.rt_split <= 4 || SMAX <= 4) topk_tokens<TPW, (SMAX < 4 ? SMAX : 4), true>(P, t0, ntok, sm);
+  else topk_tokens<TPW, SMAX, true>(P, t0, ntok, sm);
 }
 
 // K item c: top-k of kt_tok tokens.  When all tokens form one scatter chunk (n_kc == 1),

@@ -849,26 +849,41 @@ __device__ __forceinline__ void zero_item(const KParams &P, int i) {
 // activation quantisation item (fp8 activations): tokens [16 q, 16 q + 16) of the hidden rows
 // -> E4M3 codes in xq and, per 128-wide block, the exponent s (+ 127) of its power-of-two scale
 // in xs (fp8_scale_exp of the block's largest magnitude; codes of v * 2^-s, nearest even).
-// 16 lanes per block (8 values each), 16 blocks per workgroup pass; each lane issues the loads
-// of QB passes before converting any (the rows are read once, so latency is what counts).
-// Lanes past the last block repeat it (same values, so the shuffles see whole blocks) and
-// store nothing.
-constexpr int kQuantBatch = 8;
+// 16 lanes per block (8 values each), one token per 16 lanes (kQuantTokens = 16 lane groups of
+// the workgroup); each lane issues the loads of kQuantBatch blocks before converting any (the
+// rows are read once, so latency is what counts).  Lanes past the last block or token repeat
+// it (same values, so the row max sees whole blocks) and store nothing.
+constexpr int kQuantBatch = 28;
+static_assert(kQuantTokens == 4 * kWaves, "one token per 16-lane group");
+// max over the 16 lanes of a DPP row, in every lane: quad swaps (xor 1, xor 2), then the
+// mirrored half row and row (vector ALU permutes instead of four LDS-routed shuffles)
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false)));
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max<0x141>(v);  // row_half_mirror
+  return dpp_max<0x140>(v);  // row_mirror
+}
 __device__ __forceinline__ void quant_item(const KParams &P, int q) {
   const int tid = otid(), lane = tid & 63, l16 = lane & 15;
-  const int slot = (tid >> 6) * 4 + (lane >> 4);  // this lane group's block within a pass
-  const int nblk = P.d >> 7, t0 = q * kQuantTokens, nt = min(kQuantTokens, P.T - t0), nb = nt * nblk;
-  const uint16_t *x = reinterpret_cast<const uint16_t *>(P.x);
-  for (int base = 0; base < nb; base += 16 * kQuantBatch) {
+  // lane group s (16 lanes) quantises token t0 + s, kQuantBatch blocks per pass in K order
+  // (no index division); each lane holds 8 consecutive values of a 128-wide block
+  const int slot = (tid >> 6) * 4 + (lane >> 4);
+  const int nblk = P.d >> 7, t0 = q * kQuantTokens, nt = min(kQuantTokens, P.T - t0);
+  const bool live = slot < nt;
+  const size_t t = (size_t)(t0 + min(slot, nt - 1));  // (rows past the end repeat the last)
+  const uint16_t *xr = reinterpret_cast<const uint16_t *>(P.x) + t * P.d + 8 * l16;
+  uint8_t *qr = P.xq + t * P.d + 8 * l16;
+  for (int kb0 = 0; kb0 < nblk; kb0 += kQuantBatch) {
     uint4 v[kQuantBatch];
 #pragma unroll
-    for (int u = 0; u < kQuantBatch; ++u) {
-      const int blk = min(base + 16 * u + slot, nb - 1), t = t0 + blk / nblk, kb = blk % nblk;
-      v[u] = ld_glob16(x + (size_t)t * P.d + kb * 128 + 8 * l16);
-    }
+    for (int u = 0; u < kQuantBatch; ++u) v[u] = ld_glob16(xr + min(kb0 + u, nblk - 1) * 128);
 #pragma unroll
     for (int u = 0; u < kQuantBatch; ++u) {
-      const int blk = base + 16 * u + slot, bc = min(blk, nb - 1), t = t0 + bc / nblk, kb = bc % nblk;
+      const int kb = kb0 + u;
       const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       float f[8];
 #pragma unroll
@@ -879,14 +894,13 @@ __device__ __forceinline__ void quant_item(const KParams &P, int q) {
       float mx = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[e]));
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      mx = row_max16(mx);
       const int se = fp8_scale_exp(mx);
-      if (blk < nb) {
+      if (live && kb < nblk) {
         const uint64_t codes = (uint64_t)fp8x4(f[0], f[1], f[2], f[3], se) |
                                ((uint64_t)fp8x4(f[4], f[5], f[6], f[7], se) << 32);
-        st_coh64(P.xq + (size_t)t * P.d + kb * 128 + 8 * l16, codes);
-        if (l16 == 0) st_coh8(P.xs + (size_t)t * P.xs_stride + kb, (uint32_t)(se + 127));
+        st_coh64(qr + kb * 128, codes);
+        if (l16 == 0) st_coh8(P.xs + t * P.xs_stride + kb, (uint32_t)(se + 127));
       }
     }
   }

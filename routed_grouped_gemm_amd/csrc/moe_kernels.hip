@@ -6,13 +6,15 @@
 // section 四), one counter per partition of the workgroups, in this order:
 //
 //   Z  clear the per-m-tile dependency counters (and chunk histograms)
-//   L  router logits: 16 tokens x 16 experts per item, K split over the 4 waves (MFMA)
+//   L  router logits (MFMA): 16 tokens x 16 experts per item, K split over the 4 waves, or
+//      on the expert tile core 16-64 tokens x 128-256 experts over a part of K
 //      (Z and L take no ticket: each workgroup runs its share of them first)
 //   K  top-k + softmax over the kept logits for a group of tokens; the last K item to
 //      finish builds the plan (expert offsets, the m-tile descriptor table) and, for a
 //      batch that is one scatter chunk, scatters it
 //   SG shared-expert gate/up items (need no routing, so they overlap the routing)
 //   S  stable scatter of a chunk: perm / inv_perm (batches of several chunks)
+//   Q  fp8 activations only: quantise 16 hidden rows to E4M3 with per-block scales
 //   G  gate/up items (m-tile, H columns): gathered token rows x W_gate/W_up, SwiGLU in
 //      registers, H written once
 //   D  down items (m-tile, output columns): H rows x W_down -> Y
@@ -22,7 +24,8 @@
 //
 // A work item only ever waits for items earlier in this order.  Ticketed items were taken
 // by workgroups that are running (a workgroup holds at most its current ticket and the next
-// one it prefetched, which is larger); the Z and L items, which wait for nothing, are bound
+// one it prefetched, which is larger; a gate/up or down item's completion counter left
+// pending at its end is incremented before the workgroup waits for anything); the Z and L items, which wait for nothing, are bound
 // to workgroups, and the launch never has more workgroups than can be resident at once, so
 // each of those runs too.  So every wait ends, whatever the grid size.  Every wait is also
 // bounded in time; a timeout sets a fault flag that makes every later wait give up, so the

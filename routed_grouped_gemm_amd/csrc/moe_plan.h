@@ -221,13 +221,14 @@ inline Layout make_layout(const moe_problem *p, const Tiles *forced = nullptr) {
   L.n_lt = (int)ceil_div(T, L.tiles.rt_tokens);
   L.n_le = (int)ceil_div(E, L.tiles.rt_experts);
   // a router item's waves each issue one chunk of loads (16 steps, 512 K) per memory round
-  // trip: with few tiles and a long K, K is split over 2 or 4 items per tile so that each
-  // wave needs one chunk (each wave's part of K stays a multiple of 32).  Short K is not
-  // split: the router items are the first of the launch, and more of them only start later.
+  // trip, and one item's loads are bounded by its CU's bandwidth: with few tiles and K above
+  // 1024, K is split over 2 or 4 items per tile (each wave's part of K stays a multiple of
+  // 32; the top-k items add the parts, one 16-byte load each).  Short K is not split: the
+  // router items are the first of the launch, and more of them only start later.
   // Tile-core router items (mg > 1) split K until there are 256 items or 8 parts; each part
   // stays a multiple of 128, the longest K chunk of the tile core.
   L.tiles.rt_split = 1;
-  if (L.tiles.mg == 1 && (int64_t)L.n_lt * L.n_le < 64 && p->d > 2048)
+  if (L.tiles.mg == 1 && (int64_t)L.n_lt * L.n_le < 64 && p->d > 1024)
     L.tiles.rt_split = (p->d > 4096 && p->d % 512 == 0) ? 4 : 2;
   if (L.tiles.mg > 1)
     while (L.tiles.rt_split < kMaxRouterSplit(p->w_dtype == MOE_FP8_E4M3, L.tiles.mg) &&

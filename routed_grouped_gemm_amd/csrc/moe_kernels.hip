@@ -766,7 +766,8 @@ template <int WT, int MG> struct Smem {
       int hist[kMaxE];                         // per-expert slot counts of the chunk
       int tmp[kMaxE];                          // per-expert m-tile counts (plan)
       int scan0[kMaxE + 1];                    // offsets (plan)
-      int scan1[kMaxE + 1];                    // m-tile offsets (plan)
+      int scan1[kMaxE + 1];                    // m-tile offsets (plan); a chunk's base (scatter)
+      int mto[kMaxE + 1];                      // m-tile offsets (scatter items)
       uint32_t mask[kMaxE][kMaxChunkTokens / 32];  // tokens of the chunk that chose expert e
     } r;
     f4 red[kWaves][64];
@@ -1110,10 +1111,10 @@ __device__ __forceinline__ void wave_max_u32(uint32_t (&v)[N]) {
   for (int i = 0; i < N; ++i) v[i] = __builtin_amdgcn_readlane(v[i], 63);
 }
 
-// The plan: counts -> offsets (exclusive scan), m-tile counts -> m-tile offsets, the
-// m-tile descriptor table, and (several chunks) each chunk's per-expert base: the slots
-// of that expert in earlier chunks, written over the chunk histograms.  One workgroup.
-// from_lds: the single chunk's histogram is in sm.u.r.hist (no global round trip).
+// The plan: counts -> offsets (exclusive scan), m-tile counts -> m-tile offsets and the
+// m-tile descriptor table.  One workgroup.  from_lds: the single chunk's histogram is in
+// sm.u.r.hist (no global round trip); else the counts are the sums of the chunk histograms
+// (which the scatter items read too, for their own chunk's base).
 template <class SM>
 __device__ __forceinline__ void plan_wg(const KParams &P, SM &sm, bool from_lds) {
   const int tid = otid(), E = P.E, nkc = P.n_kc;
@@ -1129,10 +1130,7 @@ __device__ __forceinline__ void plan_wg(const KParams &P, SM &sm, bool from_lds)
 #pragma unroll
         for (int q = 0; q < 32; ++q) h[q] = (c0 + q < nkc) ? ld_coh(P.hist + (size_t)(c0 + q) * E + e) : 0;
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-          if (c0 + q < nkc) st_coh(P.hist + (size_t)(c0 + q) * E + e, run);
-          run += h[q];
-        }
+        for (int q = 0; q < 32; ++q) run += h[q];
       }
     }
     cnt[e] = run;
@@ -1636,14 +1634,33 @@ __device__ __forceinline__ void scatter_item(const KParams &P, int c, SM &sm) {
   for (int q = tid; q < ntok * k; q += kThreads) sm.u.r.ids[q] = checked_id(ld_coh(P.ids + (size_t)t0 * k + q), E);
   __syncthreads();
   chunk_masks(P, ntok, sm);
+  // from the chunk histograms (complete once every top-k item is done), the same numbers the
+  // plan holds: per expert, the rows of earlier chunks (this chunk's base), the total (whose
+  // exclusive scan is the expert offsets) and its m-tile count (scan: m-tile offsets)
+  const int nkc = P.n_kc;
   for (int e = tid; e < E; e += kThreads) {
-    sm.u.r.scan0[e] = ld_coh(P.offsets + e);
-    sm.u.r.scan1[e] = ld_coh(P.hist + (size_t)c * E + e);
-    if (P.phases & PH_FFN) sm.u.r.tmp[e] = ld_coh(P.mtoff + e);
+    int base = 0, total = 0;
+    for (int c0 = 0; c0 < nkc; c0 += 32) {
+      int h[32];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) h[q] = (c0 + q < nkc) ? ld_coh(P.hist + (size_t)(c0 + q) * E + e) : 0;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        base += c0 + q < c ? h[q] : 0;
+        total += h[q];
+      }
+    }
+    sm.u.r.scan1[e] = base;
+    sm.u.r.hist[e] = total;  // (the chunk's own counts there are no longer needed)
+    sm.u.r.tmp[e] = (total + P.bm - 1) / P.bm;
   }
   __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  if (wave == 0) wave_excl_scan(sm.u.r.hist, sm.u.r.scan0, E, lane);
+  if (wave == 1) wave_excl_scan(sm.u.r.tmp, sm.u.r.mto, E, lane);
+  __syncthreads();
   if (P.trace && tid == 0) sm.mark[1] = (uint32_t)wall_clock64();
-  chunk_scatter(P, c, ntok, sm.u.r.scan0, sm.u.r.scan1, sm.u.r.tmp, sm);
+  chunk_scatter(P, c, ntok, sm.u.r.scan0, sm.u.r.scan1, sm.u.r.mto, sm);
 }
 
 template <int WT> struct ActT { using type = uint16_t; };
@@ -2488,8 +2505,9 @@ void moe_persistent(KParams P) {
       else gateup_item<WT, MG>(P, true, i, sm, lb, pend);
       kind = K_SHGU;
     } else if (phase == 2) {
+      // (the scatter needs the chunk histograms only, complete once every top-k item is)
       flush();
-      if (n_mt < 0 && (n_mt = wg_wait_plan(P, sm)) < 0) break;
+      if (!wg_wait(ctrl + kSlotInts * C_KDONE, n_K, err, sm)) break;
       scatter_item(P, i, sm);
       wg_signal(ctrl + kSlotInts * C_SDONE);
       kind = K_SCATTER;

@@ -1715,8 +1715,9 @@ __device__ __forceinline__ void store_tile(const f4 (&v)[NFT][MG], char *slab, c
     for (int q = 0; q < 16 / RPI; ++q) {
       const int row = q * RPI + rr;
       const u32x4 x = *reinterpret_cast<const u32x4 *>(slab + row * RS + cb);
-      if (b * 16 + row < m)
-        __builtin_amdgcn_raw_buffer_store_b128(x, rs, (uint32_t)(((b * 16 + row) * ld + col0) * ES + cb), 0, kCpolSc1);
+      if (b * 16 + row < m)  // (unsigned: the offset may pass 2 GB, never 4 GB)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            x, rs, ((uint32_t)(b * 16 + row) * (uint32_t)ld + (uint32_t)col0) * (uint32_t)ES + (uint32_t)cb, 0, kCpolSc1);
     }
   }
 }

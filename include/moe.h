@@ -168,7 +168,7 @@ typedef struct {
  *           after start; 0 = none), then (workgroup << 32 |
  *           item kind); kinds: 0 clear, 1 router,
  *           2 top-k (+ plan), 3 shared gate/up, 4 scatter, 5 gate/up, 6 down, 7 combine,
- *           8 activation quantisation (MOE_AQ_FP8; numbered after the scatter items).
+ *           8 activation quantisation (MOE_AQ_FP8; numbered after the top-k items, before the scatter items).
  *           Items beyond the buffer are not recorded.  NULL (default) records nothing.
  * schedule: 0 = dynamic (work items taken from an atomic queue in the workspace),
  *           1 = static (item i is bound to workgroup i mod grid, like static expert-to-SM

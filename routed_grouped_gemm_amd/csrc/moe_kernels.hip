@@ -13,8 +13,8 @@
 //      finish builds the plan (expert offsets, the m-tile descriptor table) and, for a
 //      batch that is one scatter chunk, scatters it
 //   SG shared-expert gate/up items (need no routing, so they overlap the routing)
-//   S  stable scatter of a chunk: perm / inv_perm (batches of several chunks)
 //   Q  fp8 activations only: quantise 16 hidden rows to E4M3 with per-block scales
+//   S  stable scatter of a chunk: perm / inv_perm (batches of several chunks)
 //   G  gate/up items (m-tile, H columns): gathered token rows x W_gate/W_up, SwiGLU in
 //      registers, H written once
 //   D  down items (m-tile, output columns): H rows x W_down -> Y
@@ -108,7 +108,7 @@ struct KParams {
   int late;       // 1: gate/up and down items from the per-XCD queues, grouped order (see the kernel)
   int group_m;    // late phase: m-tiles per group
   int aq;         // 1: fp8 activations (Q items quantise the hidden rows; H is requantised)
-  int n_Q;        // activation-quantisation items (ticketed, after the scatter items)
+  int n_Q;        // activation-quantisation items (ticketed, before the scatter items)
   int xs_stride, hs_stride;  // bytes per row of the hidden / H block-scale arrays
   const void *x, *wr;
   const float *bias;
@@ -2383,10 +2383,12 @@ void moe_persistent(KParams P) {
       const int ticket = dynamic ? uni(sm.bcast[0]) : (int)blockIdx.x + step * (int)gridDim.x;
       ++step;
       // prefetch the next ticket (its value is read at the top of the next iteration), except
-      // during a top-k item: a second ticket taken then could be another top-k item, which
-      // this workgroup would start only after the current one
+      // during a top-k or quantisation item: a second ticket taken then could be another item
+      // of the same phase, which this workgroup would start only after the current one, while
+      // the phase's last item holds up the next phase
       have_next = false;
-      if (dynamic && tid == 0 && ticket >= n_K) {
+      const bool burst = ticket < n_K || (ticket >= n_K + n_SG && ticket < n_K + n_SG + n_Q);
+      if (dynamic && tid == 0 && !burst) {
         next = __hip_atomic_fetch_add(pctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         have_next = true;
       }
@@ -2396,12 +2398,12 @@ void moe_persistent(KParams P) {
         phase = 0, idx = i;
       } else if ((i -= n_K) < n_SG) {
         phase = 1, idx = i;
-      } else if ((i -= n_SG) < n_S) {
-        phase = 2, idx = i;
-      } else if ((i -= n_S) < n_Q) {
+      } else if ((i -= n_SG) < n_Q) {
         phase = 6, idx = i;
+      } else if ((i -= n_Q) < n_S) {
+        phase = 2, idx = i;
       } else {
-        i -= n_Q;
+        i -= n_S;
         if (!dyn) break;
         if (MG > 1 && P.late) {  // (16-row m-tiles never use the late phase)
           held = ticket;

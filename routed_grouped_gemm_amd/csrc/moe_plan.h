@@ -202,14 +202,14 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int ctr_words(const Layout &L) { return (int)align_up((size_t)(L.mt_routed_max + L.n_shmt + 1), 64); }
 
 // Work items of one launch, per phase, in order: Z (clear counters), L (router), K (top-k),
-// SG (shared gate/up), S (scatter), Q (fp8 activations: quantise the hidden rows); the
+// SG (shared gate/up), Q (fp8 activations: quantise the hidden rows), S (scatter); the
 // routed gate/up, down and combine items follow and are counted on the device once the plan
 // exists.  The Z and router items take no ticket (each workgroup runs its share of them
 // first); the others are handed out by ticket in this order.
 struct PhaseCounts {
   int gd_words, hist_words;  // words cleared by Z items: dependency counters, chunk histograms
   int z, l, k, sg, s;
-  int q;                     // activation-quantisation items (fp8 activations; ticketed after S)
+  int q;                     // activation-quantisation items (fp8 activations; ticketed before S)
 };
 
 inline Layout make_layout(const moe_problem *p, const Tiles *forced = nullptr) {

@@ -106,6 +106,19 @@ def test_plan_describe_reports_the_m_tile(L, kw):
     assert info["max_m_tiles"] >= min(T * k, E)
 
 
+@pytest.mark.parametrize("kw,split", [
+    (dict(T=16, d=2048, n=512, E=256, k=8), 2),                       # decode: few 16-row tiles, K > 1024
+    (dict(T=16, d=1024, n=512, E=256, k=8), 1),                       # short K: not split
+    (dict(T=1, d=7168, n=2048, E=256, k=8, n_shared=1, w="fp8"), 4),  # K > 4096: four parts
+    (dict(T=2048, d=1024, n=512, E=256, k=1), 1),                     # many tiles: not split
+    (dict(T=4096, d=2048, n=512, E=256, k=8), 4),                     # tile core: up to 256 items
+])
+def test_router_k_split_rule(L, kw, split):
+    # the router's K is split over several items when its tiles are too few to spread the
+    # router weights' loads over the GPU (the partial logits are added in part order)
+    assert moe.plan_describe(moe.problem(**kw))["router_k_split"] == split
+
+
 def test_fp8_activation_mode_rules(L):
     """act_quant: 0 or 1 (else INVALID), 1 only with fp8 weights (else UNSUPPORTED); the plan
     reports fp8 activations exactly when the m-tiles are above 16 rows."""

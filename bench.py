@@ -18,7 +18,7 @@ dominant (and only) kernel measured with HIP events on its launch stream, the
 CPU oracle timed on a bounded sample on this host (cpu_baseline), and a
 `configs` list with the same measurements for the other workloads: prefill (HBM
 and MFMA fractions), the skewed-load layer under the dynamic queue and under the
-static schedule, the large fp8 layer at T = 1 and 4096 (at 4096 also with fp8
+static schedule, the large fp8 layer at T = 1, 8, 512 and 4096 (at 4096 also with fp8
 activations), and the compute-bound points: prefill at T = 16384 and 32768, the
 large fp8 layer at T = 16384 (both activation modes).  `--configs` takes a
 comma-separated list of NAME[@T][:static][:fp8act] entries instead (:fp8act: the
@@ -43,8 +43,8 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 MALL_BYTES = 256 << 20
-DEFAULT_CONFIGS = ("prefill_bf16,skewed_bf16,skewed_bf16:static,large_fp8@1,large_fp8@4096,large_fp8@4096:fp8act,"
-                   "prefill_bf16@16384,prefill_bf16@32768,large_fp8@16384,large_fp8@16384:fp8act")
+DEFAULT_CONFIGS = ("prefill_bf16,skewed_bf16,skewed_bf16:static,large_fp8@1,large_fp8@8,large_fp8@512,large_fp8@4096,"
+                   "large_fp8@4096:fp8act,prefill_bf16@16384,prefill_bf16@32768,large_fp8@16384,large_fp8@16384:fp8act")
 
 
 def parse():
